@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE layer on one MI355X.
+
+One step = one moe_fused_forward call over the whole batch of the workload:
+dispatch (routing histogram, prefix sum, stable rank, gather + e4m3
+quantisation) -> L1 grouped GEMM with the SwiGLU*w / e4m3 epilogue -> L2
+grouped GEMM -> combine.  Inputs are seeded synthetic tensors already resident
+in HBM when the timed region starts.
+
+Prints ONE JSON line (rank 0):
+  value        whole-layer TFLOP/s = 6*R*H*I / step time (R = routed rows)
+  routed_rows_per_s
+  roofline     the dominant kernel (the L1 GEMM): algorithmic FLOP per launch
+               / its average duration from HIP events on its stream, against
+               the FP8 dense MFMA peak (the FP8 x FP4 scaled MFMA runs at the
+               FP8 rate)
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused MoE layer TFLOPS (% of FP8/FP4 MFMA peak) + routed rows/s, 1 GPU"
+PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (published)
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E (published)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="prefill",
+                   help="tiny | small | prefill | skewed | many")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle baseline sample (0 = skip)")
+    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                   help="measured HBM bytes per L1 launch (from rocprofv3 --pmc), if present")
+    return p.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not supported "
+              "(multi-GPU expert parallelism is a design note, not built)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import combine_dispatch_amd as moe
+    import moe_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    moe.lib()  # loud failure if the HIP library is missing
+
+    cfg = moe_inputs.CONFIG_BY_NAME[a.workload]
+    t0 = time.time()
+    inp = moe_inputs.config_inputs(a.workload)
+    gen_s = time.time() - t0
+    T, H, I, E, K = (inp[k] for k in ("T", "H", "I", "E", "K"))
+    R = int((inp["topk_idx"] >= 0).sum())
+    dev = "cuda:0"
+
+    def up(arr):
+        if arr.dtype == np.uint16:
+            arr = arr.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+
+    d = {k: up(inp[k]) for k in ("x", "topk_idx", "topk_w", "W1q", "S1", "W2q", "S2")}
+    ws = torch.empty(moe.moe_workspace_bytes(T, H, I, E, K), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, H), dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_fused_forward(d["x"], d["topk_idx"], d["topk_w"], d["W1q"], d["S1"], d["W2q"],
+                              d["S2"], y, ws, E=E, I=I, stream=stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` whole-layer steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(a.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = ev0.elapsed_time(ev1) / a.steps
+
+    # per-kernel durations: HIP events recorded by the library on its stream
+    # around each launch, in a second pass of the same steps
+    moe.moe_profile_start(a.steps)
+    for _ in range(a.steps):
+        step()
+    stage_ms, ncalls = moe.moe_profile_stop()
+    per_launch = {k: v / max(ncalls, 1) for k, v in stage_ms.items()}
+
+    flop = 6.0 * R * H * I
+    tflops = flop / (ms_per_step * 1e-3) / 1e12
+    rows_s = R / (ms_per_step * 1e-3)
+    l1_flop = 4.0 * R * H * I
+    l2_flop = 2.0 * R * I * H
+    l1_tflops = l1_flop / (per_launch["gemm_l1"] * 1e-3) / 1e12
+    l2_tflops = l2_flop / (per_launch["gemm_l2"] * 1e-3) / 1e12
+    # algorithmic bytes of the bandwidth-bound kernels (see the design notes)
+    disp_bytes = T * H * 2 + R * (H + H // 32) + T * K * 8 * 2
+    comb_bytes = R * H * 2 + T * H * 2 + T * K * 4
+
+    traffic = None
+    if os.path.exists(a.traffic_json):
+        try:
+            tj = json.load(open(a.traffic_json))
+            if tj.get("workload") == a.workload and tj.get("kernel") == "gemm_l1":
+                traffic = tj.get("hbm_bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 x fp4_e2m1 (ue8m0/32), fp32 accumulate",
+        "data": "synthetic (seeded; see moe_inputs)",
+        "config": {"workload": f"{a.workload}: T={T} H={H} I={I} E={E} K={K} routing={cfg['routing']}",
+                   "T": T, "H": H, "I": I, "E": E, "K": K, "routed_rows": R,
+                   "parallelism": "single GPU, all experts local"},
+        "routed_rows_per_s": round(rows_s, 1),
+        "frac_of_fp8_peak": round(tflops / PEAK_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "gemm_l1", "achieved": round(l1_tflops, 2),
+                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(l1_tflops / PEAK_TFLOPS, 4),
+                     "traffic": traffic},
+        "kernels_ms_per_launch": {k: round(v, 4) for k, v in per_launch.items()},
+        "kernels": {
+            "gemm_l2_tflops": round(l2_tflops, 2),
+            "dispatch_gbs": round(disp_bytes / (per_launch["dispatch"] * 1e-3) / 1e9, 1),
+            "combine_gbs": round(comb_bytes / (per_launch["combine"] * 1e-3) / 1e9, 1),
+            "hbm_peak_gbs": PEAK_HBM_GBS,
+        },
+        "wall_s_timed": round(wall, 4),
+        "input_gen_s": round(gen_s, 2),
+    }
+
+    if a.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(inp, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(inp, budget_s: float) -> dict:
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    whole tokens (all their routes) until the time budget is spent."""
+    import numpy as np
+
+    import oracle
+    T, H, I, K = inp["T"], inp["H"], inp["I"], inp["K"]
+    rng = np.random.default_rng(12345)
+    order = rng.permutation(T)
+    done_tok, routes = 0, 0
+    t0 = time.perf_counter()
+    for t in order:
+        oracle.forward_tokens(inp, [int(t)])
+        done_tok += 1
+        routes += int((inp["topk_idx"][t] >= 0).sum())
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    flop = 6.0 * routes * H * I
+    return {"value": round(flop / el / 1e12, 6), "unit": "TFLOP/s",
+            "routed_rows_per_s": round(routes / el, 3), "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done_tok} tokens ({routes} routed rows) of the same workload, "
+                      f"per-token brute-force path, {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,391 @@
+// api.hip -- the C ABI declared in include/moe.h: argument checks, workspace
+// carving and the launch sequence.  No allocation, no host synchronisation
+// (except the opt-in debug validation).
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/moe.h"
+#include "../../include/moe_profile.h"
+#include "moe_kernels.hpp"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t seg_hist, seg_base, seg_err, counts, offsets, mtiles, num_mtiles, err_flag;
+    size_t pool_src, slot_to_pool, pool_w, pool_q, pool_s, act_q, act_s, l2_out;
+    size_t routing_end;  // bytes moe_dispatch needs
+    size_t total;
+    int64_t cap;         // pool rows incl. tile padding
+    int64_t nseg;
+    int64_t max_mtiles;
+};
+
+bool shape_basic_ok(const moe_shape_t* s) {
+    return s && s->T >= 0 && s->H > 0 && s->I > 0 && s->E >= 1 && s->E <= 1024 && s->K >= 1 &&
+           s->K <= 64 && (int64_t)s->T * s->K < (int64_t(1) << 31);
+}
+
+// Workspace regions, in order.  The routing scratch comes first so that
+// moe_dispatch can use a prefix of the same layout.
+Layout make_layout(const moe_shape_t* s) {
+    Layout L;
+    const int64_t TK = (int64_t)s->T * s->K;
+    const int64_t E = s->E;
+    L.nseg = (TK + kSegSlots - 1) / kSegSlots;
+    L.max_mtiles = TK / kBM + (E < TK ? E : TK) + 1;
+    L.cap = TK + kBM;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    L.seg_hist = take(sizeof(int32_t) * L.nseg * E);
+    L.seg_base = take(sizeof(int32_t) * L.nseg * E);
+    L.seg_err = take(sizeof(int32_t) * (L.nseg + 1));
+    L.mtiles = take(sizeof(MTile) * L.max_mtiles);
+    L.num_mtiles = take(sizeof(int32_t));
+    L.err_flag = take(sizeof(int32_t));
+    L.routing_end = o;
+    L.counts = take(sizeof(int32_t) * E);
+    L.offsets = take(sizeof(int32_t) * (E + 1));
+    L.pool_src = take(sizeof(int32_t) * L.cap);
+    L.slot_to_pool = take(sizeof(int32_t) * (TK + 1));
+    L.pool_w = take(sizeof(float) * L.cap);
+    L.pool_q = take((size_t)L.cap * s->H);
+    L.pool_s = take((size_t)L.cap * (s->H / 32));
+    L.act_q = take((size_t)L.cap * s->I);
+    L.act_s = take((size_t)L.cap * (s->I / 32));
+    L.l2_out = take((size_t)L.cap * s->H * 2);
+    L.total = o;
+    return L;
+}
+
+// gfx950 check, cached per device.
+int device_ok() {
+    static int cache[64];  // 0 unknown, 1 ok, 2 bad
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64 && cache[dev]) return cache[dev] == 1;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+    const int ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) cache[dev] = ok ? 1 : 2;
+    return ok;
+}
+
+int launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+// ---- optional per-kernel timing (moe_profile.h) ------------------------------
+struct Profile {
+    bool on = false;
+    int max_calls = 0;
+    int ncalls = 0;
+    std::vector<hipEvent_t> ev;  // (MOE_PROFILE_STAGES + 1) per call
+};
+Profile g_prof;
+constexpr int kMarks = MOE_PROFILE_STAGES + 1;
+
+// Slot of this call, or -1 when not profiling.
+int prof_begin(hipStream_t stream) {
+    if (!g_prof.on || g_prof.ncalls >= g_prof.max_calls) return -1;
+    const int c = g_prof.ncalls++;
+    (void)hipEventRecord(g_prof.ev[c * kMarks], stream);
+    return c;
+}
+
+void prof_mark(int call, int stage, hipStream_t stream) {
+    if (call >= 0) (void)hipEventRecord(g_prof.ev[call * kMarks + stage + 1], stream);
+}
+
+int bits_for(int E) {
+    int b = 0;
+    while ((1 << b) < E) ++b;
+    return b < 1 ? 1 : b;
+}
+
+// a1-a3 into caller-visible arrays; the segment scratch lives at ws.
+int run_routing(const moe_shape_t* s, const Layout& L, const int64_t* topk_idx, const float* topk_w,
+                uint8_t* ws, int32_t* counts, int32_t* offsets, int32_t* pool_src,
+                int32_t* slot_to_pool, float* pool_w, hipStream_t stream, int pc = -1) {
+    const int64_t TK = (int64_t)s->T * s->K;
+    const int E = s->E;
+    const int nblk = (int)((L.nseg + kRouteWaves - 1) / kRouteWaves);
+    const size_t lds = sizeof(int32_t) * kRouteWaves * E;
+    int32_t* seg_hist = reinterpret_cast<int32_t*>(ws + L.seg_hist);
+    int32_t* seg_base = reinterpret_cast<int32_t*>(ws + L.seg_base);
+    int32_t* seg_err = reinterpret_cast<int32_t*>(ws + L.seg_err);
+    hipLaunchKernelGGL(k_route_count, dim3(nblk), dim3(kRouteThreads), lds, stream, topk_idx, TK,
+                       E, seg_hist, seg_err);
+    prof_mark(pc, MOE_STAGE_ROUTE_COUNT, stream);
+    const int scan_threads = ((E + 63) / 64) * 64;
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(scan_threads), 0, stream, seg_hist, seg_err,
+                       (int)L.nseg, E, seg_base, counts, offsets,
+                       reinterpret_cast<MTile*>(ws + L.mtiles),
+                       reinterpret_cast<int32_t*>(ws + L.num_mtiles),
+                       reinterpret_cast<int32_t*>(ws + L.err_flag));
+    prof_mark(pc, MOE_STAGE_ROUTE_SCAN, stream);
+    hipLaunchKernelGGL(k_route_scatter, dim3(nblk), dim3(kRouteThreads), lds, stream, topk_idx,
+                       topk_w, TK, E, bits_for(E), seg_base, pool_src, slot_to_pool, pool_w);
+    prof_mark(pc, MOE_STAGE_ROUTE_SCATTER, stream);
+    return launch_status();
+}
+
+int check_routing_flag(uint8_t* ws, const Layout& L, hipStream_t stream) {
+    int32_t flag = 0;
+    if (hipMemcpyAsync(&flag, ws + L.err_flag, sizeof flag, hipMemcpyDeviceToHost, stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return MOE_ERR_DEVICE;
+    return flag ? MOE_ERR_BAD_ROUTING : MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_options_t moe_default_options(void) {
+    moe_options_t o;
+    o.fast_math = 1;
+    o.activation_clamp = NAN;
+    o.debug_validate = 0;
+    return o;
+}
+
+size_t moe_workspace_bytes(const moe_shape_t* s) {
+    if (!shape_basic_ok(s) || s->H % 32 || s->I % 32) return 0;
+    return make_layout(s).total;
+}
+
+size_t moe_dispatch_workspace_bytes(const moe_shape_t* s) {
+    if (!shape_basic_ok(s) || s->H % 32) return 0;
+    moe_shape_t t = *s;
+    if (t.I % 32) t.I = 32;
+    return make_layout(&t).routing_end;
+}
+
+int moe_workspace_views(const moe_shape_t* s, moe_workspace_views_t* v) {
+    if (!v) return MOE_ERR_INVALID_ARG;
+    if (!shape_basic_ok(s) || s->H % 32 || s->I % 32) {
+        memset(v, 0xFF, sizeof *v);
+        return MOE_ERR_INVALID_ARG;
+    }
+    const Layout L = make_layout(s);
+    v->counts = (int64_t)L.counts;
+    v->offsets = (int64_t)L.offsets;
+    v->pool_src = (int64_t)L.pool_src;
+    v->slot_to_pool = (int64_t)L.slot_to_pool;
+    v->pool_w = (int64_t)L.pool_w;
+    v->pool_q = (int64_t)L.pool_q;
+    v->pool_s = (int64_t)L.pool_s;
+    v->act_q = (int64_t)L.act_q;
+    v->act_s = (int64_t)L.act_s;
+    v->l2_out = (int64_t)L.l2_out;
+    v->capacity_rows = L.cap;
+    return MOE_OK;
+}
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size or unknown payload)";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or option for the gfx950 kernels";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_DEVICE: return "device is not gfx950 or a kernel launch failed";
+        case MOE_ERR_BAD_ROUTING: return "an expert index was >= E";
+        default: return "unknown status";
+    }
+}
+
+int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
+                      const int64_t* topk_idx, const float* topk_w, const uint8_t* W1q,
+                      const uint8_t* S1, const uint8_t* W2q, const uint8_t* S2, void* y,
+                      void* workspace, size_t workspace_bytes, moe_stream_t stream_) {
+    if (!shape_basic_ok(s)) return MOE_ERR_INVALID_ARG;
+    const moe_options_t o = opt ? *opt : moe_default_options();
+    if (!isnan(o.activation_clamp)) return MOE_ERR_UNSUPPORTED;
+    if (s->H % kBN || s->I % 128) return MOE_ERR_UNSUPPORTED;
+    if (s->T == 0) return MOE_OK;
+    if (!x || !topk_idx || !topk_w || !W1q || !S1 || !W2q || !S2 || !y) return MOE_ERR_INVALID_ARG;
+    const Layout L = make_layout(s);
+    if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
+        return MOE_ERR_WORKSPACE;
+    if (!device_ok()) return MOE_ERR_DEVICE;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const int T = s->T, H = s->H, I = s->I, K = s->K;
+    int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+    int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+    int32_t* pool_src = reinterpret_cast<int32_t*>(ws + L.pool_src);
+    int32_t* slot_to_pool = reinterpret_cast<int32_t*>(ws + L.slot_to_pool);
+    float* pool_w = reinterpret_cast<float*>(ws + L.pool_w);
+    uint8_t* pool_q = ws + L.pool_q;
+    uint8_t* pool_s = ws + L.pool_s;
+    uint8_t* act_q = ws + L.act_q;
+    uint8_t* act_s = ws + L.act_s;
+    uint16_t* l2_out = reinterpret_cast<uint16_t*>(ws + L.l2_out);
+
+    const int pc = prof_begin(stream);
+    int rc = run_routing(s, L, topk_idx, topk_w, ws, counts, offsets, pool_src, slot_to_pool,
+                         pool_w, stream, pc);
+    if (rc) return rc;
+    if (o.debug_validate && (rc = check_routing_flag(ws, L, stream))) return rc;
+
+    hipLaunchKernelGGL(k_dispatch_fp8, dim3(T), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(x), H, K, slot_to_pool, pool_q, pool_s);
+    prof_mark(pc, MOE_STAGE_DISPATCH, stream);
+
+    GemmArgs g1;
+    memset(&g1, 0, sizeof g1);
+    g1.A = pool_q;
+    g1.SA = pool_s;
+    g1.B = W1q;
+    g1.SB = S1;
+    g1.mtiles = reinterpret_cast<const MTile*>(ws + L.mtiles);
+    g1.num_mtiles = reinterpret_cast<const int32_t*>(ws + L.num_mtiles);
+    g1.Kdim = H;
+    g1.N = 2 * I;
+    g1.ntiles = I / 128;
+    g1.pool_w = pool_w;
+    g1.act_q = act_q;
+    g1.act_s = act_s;
+    g1.I = I;
+    g1.fast_math = o.fast_math ? 1 : 0;
+    hipLaunchKernelGGL(k_gemm_l1, dim3((unsigned)(L.max_mtiles * g1.ntiles)), dim3(kGemmThreads),
+                       0, stream, g1);
+    prof_mark(pc, MOE_STAGE_GEMM_L1, stream);
+
+    GemmArgs g2 = g1;
+    g2.A = act_q;
+    g2.SA = act_s;
+    g2.B = W2q;
+    g2.SB = S2;
+    g2.Kdim = I;
+    g2.N = H;
+    g2.ntiles = H / kBN;
+    g2.out = l2_out;
+    hipLaunchKernelGGL(k_gemm_l2, dim3((unsigned)(L.max_mtiles * g2.ntiles)), dim3(kGemmThreads),
+                       0, stream, g2);
+    prof_mark(pc, MOE_STAGE_GEMM_L2, stream);
+
+    hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, stream, l2_out, slot_to_pool,
+                       static_cast<const float*>(nullptr), H, K, static_cast<uint16_t*>(y));
+    prof_mark(pc, MOE_STAGE_COMBINE, stream);
+    return launch_status();
+}
+
+int moe_dispatch(const moe_shape_t* s, const void* x, const int64_t* topk_idx, const float* topk_w,
+                 int payload, int32_t* counts, int32_t* offsets, int32_t* pool_src,
+                 int32_t* slot_to_pool, float* pool_w, void* pool, uint8_t* pool_scales,
+                 void* workspace, size_t workspace_bytes, moe_stream_t stream_) {
+    if (!shape_basic_ok(s)) return MOE_ERR_INVALID_ARG;
+    if (payload != MOE_PAYLOAD_FP8_E4M3 && payload != MOE_PAYLOAD_BF16) return MOE_ERR_INVALID_ARG;
+    if (s->H % 32) return MOE_ERR_UNSUPPORTED;
+    if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+    moe_shape_t t = *s;
+    if (t.I % 32) t.I = 32;
+    const Layout L = make_layout(&t);
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if (!workspace || workspace_bytes < L.routing_end ||
+        (reinterpret_cast<uintptr_t>(workspace) % kAlign))
+        return MOE_ERR_WORKSPACE;
+    if (s->T == 0) {
+        // nothing routed: one scan over zero segments writes counts = 0 and
+        // offsets = 0
+        if (!device_ok()) return MOE_ERR_DEVICE;
+        uint8_t* ws = static_cast<uint8_t*>(workspace);
+        const int scan_threads = ((s->E + 63) / 64) * 64;
+        hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(scan_threads), 0, stream,
+                           reinterpret_cast<int32_t*>(ws + L.seg_hist),
+                           reinterpret_cast<int32_t*>(ws + L.seg_err), 0, s->E,
+                           reinterpret_cast<int32_t*>(ws + L.seg_base), counts, offsets,
+                           reinterpret_cast<MTile*>(ws + L.mtiles),
+                           reinterpret_cast<int32_t*>(ws + L.num_mtiles),
+                           reinterpret_cast<int32_t*>(ws + L.err_flag));
+        return launch_status();
+    }
+    if (!x || !topk_idx || !topk_w || !pool_src || !slot_to_pool || !pool_w || !pool ||
+        (payload == MOE_PAYLOAD_FP8_E4M3 && !pool_scales))
+        return MOE_ERR_INVALID_ARG;
+    if (!device_ok()) return MOE_ERR_DEVICE;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    int rc = run_routing(s, L, topk_idx, topk_w, ws, counts, offsets, pool_src, slot_to_pool,
+                         pool_w, stream);
+    if (rc) return rc;
+    if (payload == MOE_PAYLOAD_FP8_E4M3)
+        hipLaunchKernelGGL(k_dispatch_fp8, dim3(s->T), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(x), s->H, s->K, slot_to_pool,
+                           static_cast<uint8_t*>(pool), pool_scales);
+    else
+        hipLaunchKernelGGL(k_dispatch_bf16, dim3(s->T), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(x), s->H, s->K, slot_to_pool,
+                           static_cast<uint16_t*>(pool));
+    return launch_status();
+}
+
+int moe_combine(const moe_shape_t* s, const void* pool_out, const int32_t* slot_to_pool,
+                const float* topk_w, void* y, moe_stream_t stream_) {
+    if (!shape_basic_ok(s)) return MOE_ERR_INVALID_ARG;
+    if (s->H % 8) return MOE_ERR_UNSUPPORTED;
+    if (s->T == 0) return MOE_OK;
+    if (!pool_out || !slot_to_pool || !y) return MOE_ERR_INVALID_ARG;
+    if (!device_ok()) return MOE_ERR_DEVICE;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    hipLaunchKernelGGL(k_combine, dim3(s->T), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(pool_out), slot_to_pool, topk_w, s->H, s->K,
+                       static_cast<uint16_t*>(y));
+    return launch_status();
+}
+
+int moe_profile_start(int max_calls) {
+    if (max_calls < 1 || max_calls > 4096) return MOE_ERR_INVALID_ARG;
+    for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+    g_prof = Profile();
+    g_prof.ev.resize((size_t)max_calls * kMarks);
+    for (auto& e : g_prof.ev)
+        if (hipEventCreate(&e) != hipSuccess) return MOE_ERR_DEVICE;
+    g_prof.max_calls = max_calls;
+    g_prof.on = true;
+    return MOE_OK;
+}
+
+int moe_profile_stop(double* stage_ms, int* ncalls) {
+    if (!g_prof.on || !stage_ms || !ncalls) return MOE_ERR_INVALID_ARG;
+    int rc = MOE_OK;
+    for (int k = 0; k < MOE_PROFILE_STAGES; ++k) stage_ms[k] = 0.0;
+    for (int c = 0; c < g_prof.ncalls && rc == MOE_OK; ++c) {
+        if (hipEventSynchronize(g_prof.ev[c * kMarks + MOE_PROFILE_STAGES]) != hipSuccess) {
+            rc = MOE_ERR_DEVICE;
+            break;
+        }
+        for (int k = 0; k < MOE_PROFILE_STAGES; ++k) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, g_prof.ev[c * kMarks + k], g_prof.ev[c * kMarks + k + 1]) !=
+                hipSuccess) {
+                rc = MOE_ERR_DEVICE;
+                break;
+            }
+            stage_ms[k] += ms;
+        }
+    }
+    *ncalls = g_prof.ncalls;
+    for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+    g_prof = Profile();
+    return rc;
+}
+
+const char* moe_profile_stage_name(int stage) {
+    static const char* names[MOE_PROFILE_STAGES] = {"route_count", "route_scan", "route_scatter",
+                                                    "dispatch", "gemm_l1", "gemm_l2", "combine"};
+    return stage >= 0 && stage < MOE_PROFILE_STAGES ? names[stage] : "?";
+}
+
+}  // extern "C"

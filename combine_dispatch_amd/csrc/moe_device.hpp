@@ -1,0 +1,81 @@
+// moe_device.hpp -- device-side helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// bf16 bits -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
+
+// Two fp32 -> packed bf16x2, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    f2 v = {lo, hi};
+    bf2 r = __builtin_convertvector(v, bf2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// fp32 -> bf16 -> fp32 (the rounding the GEMM epilogue applies).
+__device__ __forceinline__ float round_bf16(float v) {
+    return __uint_as_float(pack_bf16x2(v, 0.f) << 16);
+}
+
+// Two fp32 -> two e4m3 bytes in the low half (v_cvt_pk_fp8_f32, OCP e4m3fn,
+// round to nearest even).
+__device__ __forceinline__ uint32_t pack_fp8x2(float a, float b) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Four fp32 -> four e4m3 bytes.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// UE8M0 scale byte for an e4m3 group: the smallest b with
+// amax <= 448 * 2^(b-127), from the fp32 fields of amax: exponent field
+// minus 8, plus one when the significand exceeds 1.75 (448 = 1.75 * 2^8).
+__device__ __forceinline__ uint32_t ue8m0_e4m3(float amax) {
+    const uint32_t bits = __float_as_uint(amax);
+    int b = (int)((bits >> 23) & 0xFFu) - 8 + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    b = b < 0 ? 0 : (b > 254 ? 254 : b);
+    return (uint32_t)b;
+}
+
+// v * 2^(127-b): exact (v_ldexp_f32).
+__device__ __forceinline__ float unscale(float v, uint32_t b) {
+    return __builtin_amdgcn_ldexpf(v, 127 - (int)b);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Max over the 4 lanes of an aligned quad (DPP quad permutes).
+__device__ __forceinline__ float quad_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    return v;
+}
+
+// Max over the 32 lanes of each wave half.
+__device__ __forceinline__ float half_wave_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, __shfl_xor(v, 8));
+    v = fmaxf(v, __shfl_xor(v, 16));
+    return v;
+}
+
+}  // namespace moe

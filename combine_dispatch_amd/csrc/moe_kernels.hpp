@@ -1,0 +1,77 @@
+// moe_kernels.hpp -- kernel entry points and launch constants shared between
+// the kernel sources and the host API.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Routing: one wave owns a segment of kSegSlots consecutive flat slots.
+constexpr int kSegSlots = 1024;
+constexpr int kRouteWaves = 4;  // waves per routing block
+constexpr int kRouteThreads = kRouteWaves * 64;
+
+// Grouped GEMM tiling: 256 x 256 output tile per 256-thread workgroup,
+// 128 K per main-loop step, two LDS stages.
+constexpr int kBM = 256;
+constexpr int kBN = 256;
+constexpr int kBK = 128;
+constexpr int kGemmThreads = 256;
+constexpr int kStageA = kBM * kBK;          // e4m3 bytes
+constexpr int kStageB = kBN * kBK / 2;      // e2m1 bytes
+constexpr int kStageSA = kBM * 4;           // 4 scale bytes per row per step
+constexpr int kStageSB = kBN * 4;
+constexpr int kStageBytes = kStageA + kStageB + kStageSA + kStageSB;
+constexpr int kStages = 2;
+constexpr int kGemmLds = kStages * kStageBytes + kBM * 4;  // + routing weights
+
+struct MTile {
+    int32_t expert, row0, nrows, pad;
+};
+
+struct GemmArgs {
+    const uint8_t* A;    // e4m3 [rows][Kdim]
+    const uint8_t* SA;   // ue8m0 [rows][Kdim/32]
+    const uint8_t* B;    // e2m1x2 [E][N][Kdim/2]
+    const uint8_t* SB;   // ue8m0 [E][N][Kdim/32]
+    const MTile* mtiles;
+    const int32_t* num_mtiles;
+    int32_t Kdim;        // reduction size
+    int32_t N;           // output columns per expert of B (L1: 2I, L2: H)
+    int32_t ntiles;      // workgroup tiles along N
+    // L1 epilogue
+    const float* pool_w; // [rows]
+    uint8_t* act_q;      // e4m3 [rows][I]
+    uint8_t* act_s;      // ue8m0 [rows][I/32]
+    int32_t I;
+    int32_t fast_math;
+    // L2 epilogue
+    uint16_t* out;       // bf16 [rows][N]
+};
+
+__global__ void k_route_count(const int64_t* __restrict__ topk_idx, int64_t TK, int E,
+                              int32_t* __restrict__ seg_hist, int32_t* __restrict__ seg_err);
+__global__ void k_route_scan(const int32_t* __restrict__ seg_hist,
+                             const int32_t* __restrict__ seg_err, int nseg, int E,
+                             int32_t* __restrict__ seg_base, int32_t* __restrict__ counts,
+                             int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
+                             int32_t* __restrict__ num_mtiles, int32_t* __restrict__ err_flag);
+__global__ void k_route_scatter(const int64_t* __restrict__ topk_idx,
+                                const float* __restrict__ topk_w, int64_t TK, int E, int nbits,
+                                const int32_t* __restrict__ seg_base,
+                                int32_t* __restrict__ pool_src,
+                                int32_t* __restrict__ slot_to_pool, float* __restrict__ pool_w);
+__global__ void k_dispatch_fp8(const uint16_t* __restrict__ x, int H, int K,
+                               const int32_t* __restrict__ slot_to_pool,
+                               uint8_t* __restrict__ pool, uint8_t* __restrict__ pool_s);
+__global__ void k_dispatch_bf16(const uint16_t* __restrict__ x, int H, int K,
+                                const int32_t* __restrict__ slot_to_pool,
+                                uint16_t* __restrict__ pool);
+__global__ void k_combine(const uint16_t* __restrict__ o, const int32_t* __restrict__ slot_to_pool,
+                          const float* __restrict__ topk_w, int H, int K,
+                          uint16_t* __restrict__ y);
+__global__ void k_gemm_l1(GemmArgs args);
+__global__ void k_gemm_l2(GemmArgs args);
+
+}  // namespace moe

@@ -1,0 +1,286 @@
+// route.hip -- dispatch (a1-a4) and combine (a9) kernels for gfx950.
+//
+// Dispatch follows the counting-sort shape the pages describe for the
+// dispatch warps (page "Dispatch/Combine in Mega MoE", sections 3.1 and 8.3;
+// page "DeepEP -> Mega MoE", "dispatch.cuh" snippets): a per-expert count of
+// topk_idx, an exclusive prefix sum into per-expert offsets, a slot inside the
+// expert, then a copy of the token row into that expert-major pool slot.
+// Differences from the pages' design, for one GPU and a deterministic result:
+//  - slots are ranked stably (ascending flat slot t*K+k inside an expert)
+//    instead of by atomic arrival order;
+//  - the histogram is privatised per wave in LDS over fixed 1024-slot
+//    segments, so the ranking pass can start each segment from an exact base;
+//  - the token row is quantised to e4m3 while it is copied (the pages pull
+//    rows that are already FP8; quantising per row before or after the copy
+//    gives the same bytes).
+#include "moe_device.hpp"
+#include "moe_kernels.hpp"
+
+namespace moe {
+
+// a1: per-segment expert histogram.  One wave per 1024-slot segment, LDS
+// atomics on a per-wave histogram.  Indices >= E are counted as errors and
+// otherwise treated as masked.
+__global__ __launch_bounds__(kRouteThreads) void k_route_count(
+    const int64_t* __restrict__ topk_idx, int64_t TK, int E, int32_t* __restrict__ seg_hist,
+    int32_t* __restrict__ seg_err) {
+    extern __shared__ int32_t lds_hist[];  // [kRouteWaves][E]
+    const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t nseg = (TK + kSegSlots - 1) / kSegSlots;
+    const int64_t seg = (int64_t)blockIdx.x * kRouteWaves + wv;
+    int32_t* h = lds_hist + wv * E;
+    for (int e = lane; e < E; e += kWave) h[e] = 0;
+    __syncthreads();
+    int bad = 0;
+    if (seg < nseg) {
+        const int64_t f0 = seg * kSegSlots;
+        for (int i = lane; i < kSegSlots; i += kWave) {
+            const int64_t f = f0 + i;
+            if (f >= TK) break;
+            const int64_t e = topk_idx[f];
+            if (e >= E)
+                bad = 1;
+            else if (e >= 0)
+                atomicAdd(&h[e], 1);
+        }
+    }
+    __syncthreads();
+    if (seg < nseg) {
+        for (int e = lane; e < E; e += kWave) seg_hist[seg * E + e] = h[e];
+        const unsigned long long any_bad = __ballot(bad);
+        if (lane == 0) seg_err[seg] = any_bad ? 1 : 0;
+    }
+}
+
+// a2: exclusive prefix sum.  One block, thread e owns expert e: it walks the
+// segments (per-segment bases inside the expert), then a block-wide scan over
+// experts gives offsets[E+1]; the same scan over ceil(count/kBM) lays out the
+// GEMM's expert-major m-tile table.
+__global__ __launch_bounds__(1024) void k_route_scan(
+    const int32_t* __restrict__ seg_hist, const int32_t* __restrict__ seg_err, int nseg, int E,
+    int32_t* __restrict__ seg_base, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    MTile* __restrict__ mtiles, int32_t* __restrict__ num_mtiles, int32_t* __restrict__ err_flag) {
+    __shared__ int32_t wsum[16], wsum_t[16], werr[16];
+    const int e = threadIdx.x;
+    const int lane = e % kWave, wv = e / kWave;
+    int run = 0, err = 0;
+    if (e < E) {
+        for (int s = 0; s < nseg; ++s) {
+            const int v = seg_hist[(int64_t)s * E + e];
+            seg_base[(int64_t)s * E + e] = run;
+            run += v;
+        }
+    }
+    for (int s = e; s < nseg; s += blockDim.x) err |= seg_err[s];
+    const int cnt = e < E ? run : 0;
+    const int nt = (cnt + kBM - 1) / kBM;
+    int inc = cnt, inc_t = nt;
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int a = __shfl_up(inc, d), b = __shfl_up(inc_t, d);
+        if (lane >= d) {
+            inc += a;
+            inc_t += b;
+        }
+    }
+    const unsigned long long eb = __ballot(err);
+    if (lane == kWave - 1) {
+        wsum[wv] = inc;
+        wsum_t[wv] = inc_t;
+    }
+    if (lane == 0) werr[wv] = eb ? 1 : 0;
+    __syncthreads();
+    int base = 0, base_t = 0, any_err = 0;
+    for (int i = 0; i < (int)(blockDim.x / kWave); ++i) {
+        if (i < wv) {
+            base += wsum[i];
+            base_t += wsum_t[i];
+        }
+        any_err |= werr[i];
+    }
+    const int off = base + inc - cnt;
+    const int toff = base_t + inc_t - nt;
+    if (e < E) {
+        counts[e] = cnt;
+        offsets[e] = off;
+        for (int s = 0; s < nseg; ++s) seg_base[(int64_t)s * E + e] += off;
+        for (int i = 0; i < nt; ++i) {
+            MTile m;
+            m.expert = e;
+            m.row0 = off + i * kBM;
+            m.nrows = min(kBM, cnt - i * kBM);
+            m.pad = 0;
+            mtiles[toff + i] = m;
+        }
+    }
+    if (e == E - 1) {
+        offsets[E] = off + cnt;
+        *num_mtiles = toff + nt;
+        *err_flag = any_err;
+    }
+}
+
+// a3: stable rank.  Each wave walks its segment 64 slots at a time; lanes
+// holding the same expert find each other with one ballot per index bit, the
+// lower lanes go first, and one lane advances the expert's running base in
+// LDS.  The segment bases come from k_route_scan, so pool rows come out in
+// ascending flat-slot order inside every expert.
+__global__ __launch_bounds__(kRouteThreads) void k_route_scatter(
+    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int64_t TK, int E,
+    int nbits, const int32_t* __restrict__ seg_base, int32_t* __restrict__ pool_src,
+    int32_t* __restrict__ slot_to_pool, float* __restrict__ pool_w) {
+    extern __shared__ int32_t lds_run[];  // [kRouteWaves][E]
+    const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t nseg = (TK + kSegSlots - 1) / kSegSlots;
+    const int64_t seg = (int64_t)blockIdx.x * kRouteWaves + wv;
+    int32_t* run = lds_run + wv * E;
+    if (seg < nseg)
+        for (int e = lane; e < E; e += kWave) run[e] = seg_base[seg * E + e];
+    __syncthreads();
+    if (seg >= nseg) return;
+    const unsigned long long lt_mask = (1ull << lane) - 1ull;
+    const int64_t f0 = seg * kSegSlots;
+    for (int it = 0; it < kSegSlots / kWave; ++it) {
+        const int64_t f = f0 + it * kWave + lane;
+        if (f0 + it * kWave >= TK) break;  // wave-uniform
+        int e = -1;
+        float w = 0.f;
+        if (f < TK) {
+            const int64_t v = topk_idx[f];
+            if (v >= 0 && v < E) {
+                e = (int)v;
+                w = topk_w[f];
+            }
+        }
+        unsigned long long peers = __ballot(e >= 0);
+        for (int b = 0; b < nbits; ++b) {
+            const int bit = (e >> b) & 1;
+            const unsigned long long set = __ballot(bit);
+            peers &= bit ? set : ~set;
+        }
+        if (e >= 0) {
+            const int base = run[e];
+            const int r = base + __popcll(peers & lt_mask);
+            pool_src[r] = (int32_t)f;
+            slot_to_pool[f] = r;
+            pool_w[r] = w;
+            if ((peers >> lane) == 1ull) run[e] = base + __popcll(peers);  // highest peer lane
+        } else if (f < TK) {
+            slot_to_pool[f] = -1;
+        }
+    }
+}
+
+// a4: gather + quantise.  One block per token row.  Each lane owns 8
+// consecutive columns (one 16-byte load), a quad of lanes owns one 32-column
+// scale group: amax over the quad, UE8M0 scale, e4m3 codes, then the 8 code
+// bytes go to every valid pool row of the token.
+__global__ __launch_bounds__(256) void k_dispatch_fp8(const uint16_t* __restrict__ x, int H,
+                                                     int K, const int32_t* __restrict__ slot_to_pool,
+                                                     uint8_t* __restrict__ pool,
+                                                     uint8_t* __restrict__ pool_s) {
+    __shared__ int32_t rows[64];
+    const int64_t t = blockIdx.x;
+    if (threadIdx.x < K) rows[threadIdx.x] = slot_to_pool[t * K + threadIdx.x];
+    __syncthreads();
+    const uint16_t* xr = x + t * H;
+    for (int c0 = threadIdx.x * 8; c0 < H; c0 += 256 * 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xr + c0);
+        float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+        amax = quad_max(amax);
+        const uint32_t b = ue8m0_e4m3(amax);
+        uint2 q;
+        q.x = pack_fp8x4(unscale(f[0], b), unscale(f[1], b), unscale(f[2], b), unscale(f[3], b));
+        q.y = pack_fp8x4(unscale(f[4], b), unscale(f[5], b), unscale(f[6], b), unscale(f[7], b));
+        for (int k = 0; k < K; ++k) {
+            const int32_t r = rows[k];
+            if (r < 0) continue;
+            *reinterpret_cast<uint2*>(pool + (int64_t)r * H + c0) = q;
+            if ((threadIdx.x & 3) == 0) pool_s[(int64_t)r * (H / 32) + c0 / 32] = (uint8_t)b;
+        }
+    }
+}
+
+// a4 with a bf16 payload: plain row copies (for callers that run their own
+// expert GEMM on bf16 rows).
+__global__ __launch_bounds__(256) void k_dispatch_bf16(const uint16_t* __restrict__ x, int H,
+                                                      int K, const int32_t* __restrict__ slot_to_pool,
+                                                      uint16_t* __restrict__ pool) {
+    __shared__ int32_t rows[64];
+    const int64_t t = blockIdx.x;
+    if (threadIdx.x < K) rows[threadIdx.x] = slot_to_pool[t * K + threadIdx.x];
+    __syncthreads();
+    const uint16_t* xr = x + t * H;
+    for (int c0 = threadIdx.x * 8; c0 < H; c0 += 256 * 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xr + c0);
+        for (int k = 0; k < K; ++k) {
+            const int32_t r = rows[k];
+            if (r >= 0) *reinterpret_cast<uint4*>(pool + (int64_t)r * H + c0) = v;
+        }
+    }
+}
+
+// a9: combine.  One block per token; each lane owns 8 columns.  The K pool
+// rows of the token are loaded first (independent loads in flight), then
+// summed in ascending k in fp32 starting from +0, then rounded to bf16.
+// Multiplies and adds stay separately rounded.
+#pragma clang fp contract(off)
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
+                                                const int32_t* __restrict__ slot_to_pool,
+                                                const float* __restrict__ topk_w, int H, int K,
+                                                uint16_t* __restrict__ y) {
+    __shared__ int32_t rows[64];
+    __shared__ float wts[64];
+    const int64_t t = blockIdx.x;
+    if (threadIdx.x < K) {
+        rows[threadIdx.x] = slot_to_pool[t * K + threadIdx.x];
+        wts[threadIdx.x] = topk_w ? topk_w[t * K + threadIdx.x] : 1.0f;
+    }
+    __syncthreads();
+    for (int c0 = threadIdx.x * 8; c0 < H; c0 += 256 * 8) {
+        float acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+        for (int k0 = 0; k0 < K; k0 += 8) {
+            uint4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int k = k0 + u;
+                const int32_t r = k < K ? rows[k] : -1;
+                v[u] = r >= 0 ? *reinterpret_cast<const uint4*>(o + (int64_t)r * H + c0)
+                              : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int k = k0 + u;
+                if (k >= K || rows[k] < 0) continue;
+                const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                if (topk_w) {
+                    const float wk = wts[k];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc[2 * j] = acc[2 * j] + bf16_lo(w4[j]) * wk;
+                        acc[2 * j + 1] = acc[2 * j + 1] + bf16_hi(w4[j]) * wk;
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc[2 * j] = acc[2 * j] + bf16_lo(w4[j]);
+                        acc[2 * j + 1] = acc[2 * j + 1] + bf16_hi(w4[j]);
+                    }
+                }
+            }
+        }
+        uint4 out;
+        out.x = pack_bf16x2(acc[0], acc[1]);
+        out.y = pack_bf16x2(acc[2], acc[3]);
+        out.z = pack_bf16x2(acc[4], acc[5]);
+        out.w = pack_bf16x2(acc[6], acc[7]);
+        *reinterpret_cast<uint4*>(y + t * H + c0) = out;
+    }
+}
+
+}  // namespace moe

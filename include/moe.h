@@ -1,0 +1,173 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE layer library, libmoe_hip.so.
+ *
+ * One MoE layer's data-parallel hot path on one GPU: token dispatch into an
+ * expert-major pool, the L1 grouped GEMM (FP8 e4m3 activations x FP4 e2m1
+ * weights, one UE8M0 scale per 32 along K on both operands), SwiGLU scaled by
+ * the routing weight and requantised to FP8, the L2 grouped GEMM, and the
+ * fp32 top-k combine back to token-major bf16.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] "DeepEP -> Mega MoE: the evolving boundary of communication and
+ *        compute" -- code-snippet headings, no numbered sections.
+ *   [P2] "Normal vs Low-Latency: DeepEP's two communication philosophies
+ *        mapped onto Mega MoE", sections 1-12.
+ *   [P3] "Dispatch/Combine in the DeepGEMM Mega MoE kernel", sections 1-9,
+ *        appendix A.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers, row-major, densely packed.  The
+ *     caller owns every buffer; the library never allocates.
+ *   - Calls are asynchronous on `stream` (NULL = the default stream) and never
+ *     synchronise the host, except moe_options_t.debug_validate.
+ *   - Return MOE_OK (0) or a negative status.  Shape, pointer and workspace
+ *     errors are found on the host before anything is launched; a failed
+ *     launch returns MOE_ERR_DEVICE.  Faults inside a kernel surface at the
+ *     caller's next synchronisation, as usual for HIP.
+ *   - T == 0 is valid and launches nothing.
+ *   - Expert indices: a negative value marks a masked slot ([P3] section 4.1).
+ *     An index >= E is a caller error: the kernels treat it as masked (they
+ *     never index out of bounds with it) and raise a device flag that
+ *     debug_validate turns into MOE_ERR_BAD_ROUTING.
+ *
+ * Number formats: bf16 = the top 16 bits of an IEEE binary32; e4m3 = OCP
+ * e4m3fn bytes; e2m1 = OCP FP4, two codes per byte, the even K index in the
+ * low nibble; ue8m0 = a scale byte b standing for 2^(b-127).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* moe_stream_t; /* a hipStream_t */
+
+typedef struct {
+    int32_t T; /* tokens, >= 0 */
+    int32_t H; /* hidden size: L1 K and L2 N; multiple of 256 */
+    int32_t I; /* intermediate size: L1 N = 2I (gate | up), L2 K; multiple of 128 */
+    int32_t E; /* experts on this GPU, 1..1024 */
+    int32_t K; /* top-k slots per token, 1..64 */
+} moe_shape_t;
+
+typedef struct {
+    int32_t fast_math;        /* 1 (default): hardware exp and reciprocal in SwiGLU;
+                                 0: library expf and IEEE division */
+    float activation_clamp;   /* NaN (default) = none; any other value -> MOE_ERR_UNSUPPORTED */
+    int32_t debug_validate;   /* 1: synchronise after routing and return
+                                 MOE_ERR_BAD_ROUTING if an expert index was >= E */
+} moe_options_t;
+
+enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* null pointer, negative size, unknown payload */
+    MOE_ERR_UNSUPPORTED = -2, /* shape outside the kernels' tiling, option not implemented */
+    MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+    MOE_ERR_DEVICE = -4,      /* not a gfx950 device, or a launch failed */
+    MOE_ERR_BAD_ROUTING = -5  /* debug_validate found an expert index >= E */
+};
+
+enum { MOE_PAYLOAD_FP8_E4M3 = 0, MOE_PAYLOAD_BF16 = 1 };
+
+/* Defaults: fast_math 1, activation_clamp NaN, debug_validate 0. */
+moe_options_t moe_default_options(void);
+
+/* Bytes of device workspace moe_fused_forward needs for shape *s (capacity
+ * T*K routed rows plus tile padding).  Host only; 0 on a bad shape. */
+size_t moe_workspace_bytes(const moe_shape_t* s);
+
+/* Bytes of device workspace moe_dispatch needs (routing scratch only). */
+size_t moe_dispatch_workspace_bytes(const moe_shape_t* s);
+
+/*
+ * The whole layer, y = combine(L2(requant(SwiGLU(L1(dispatch(x))) * w))).
+ * Steps: [P3] sections 3-5 (dispatch warps, L1 epilogue with SwiGLU and the
+ * routing weight, L2, combine); [P1] "complete compute pipeline" snippet
+ * (GEMM, SwiGLU, amax, FP8 requant, top-k reduction); the layer's entry with
+ * y first and a caller-allocated buffer, [P2] section 2.
+ *
+ *   x         bf16  [T][H]
+ *   topk_idx  int64 [T][K]   expert per slot; < 0 masked
+ *   topk_w    fp32  [T][K]   routing weights (applied to the SwiGLU output)
+ *   W1q       e2m1x2 [E][2I][H/2]  rows 0..I-1 gate, I..2I-1 up
+ *   S1        ue8m0 [E][2I][H/32]
+ *   W2q       e2m1x2 [E][H][I/2]
+ *   S2        ue8m0 [E][H][I/32]
+ *   y         bf16  [T][H], fully overwritten (an all-masked token gives +0)
+ *   workspace device buffer of at least moe_workspace_bytes(s) bytes, 256-byte
+ *             aligned; its contents on entry do not matter.
+ * Numerics: x is quantised per token row in groups of 32 (scale = smallest
+ * power of two with amax <= 448 * scale, e4m3 round-to-nearest-even); GEMM
+ * outputs are fp32 sums rounded to bf16; SwiGLU is silu(gate) * up * w in
+ * fp32, requantised the same way per 32 along I; combine sums the slots' bf16
+ * rows in fp32 in ascending k, then rounds to bf16.
+ * Shapes: H % 256 == 0, I % 128 == 0, 1 <= E <= 1024, 1 <= K <= 64,
+ * T * K < 2^31.  Otherwise MOE_ERR_UNSUPPORTED.
+ */
+int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt /* NULL = defaults */,
+                      const void* x, const int64_t* topk_idx, const float* topk_w,
+                      const uint8_t* W1q, const uint8_t* S1, const uint8_t* W2q,
+                      const uint8_t* S2, void* y, void* workspace, size_t workspace_bytes,
+                      moe_stream_t stream);
+
+/*
+ * Dispatch only: routing metadata plus the expert-major pool.  [P3] sections
+ * 3.1-3.2 and appendix A.2; [P1] "dispatch.cuh" snippets (per-expert count,
+ * prefix sum, slot allocation, row copy).
+ *   counts        int32 [E]     rows per expert
+ *   offsets       int32 [E+1]   exclusive prefix sum; offsets[E] = R
+ *   pool_src      int32 [T*K]   flat slot t*K+k of pool row r (first R entries)
+ *   slot_to_pool  int32 [T*K]   pool row of slot t*K+k, -1 if masked
+ *   pool_w        fp32  [T*K]   topk_w of pool row r (first R entries)
+ *   pool          [T*K][H]      payload MOE_PAYLOAD_FP8_E4M3: e4m3 codes;
+ *                               MOE_PAYLOAD_BF16: bf16 copies of x rows
+ *   pool_scales   ue8m0 [T*K][H/32] (FP8 payload only; NULL for bf16)
+ * Pool order is canonical: expert-major, and inside an expert ascending flat
+ * slot t*K+k (the pages assign slots with atomics, so their order is not
+ * fixed; this one is deterministic).  Rows past R are not written.
+ * Shapes: H % 32 == 0 (H % 256 not required here), 1 <= E <= 1024.
+ */
+int moe_dispatch(const moe_shape_t* s, const void* x, const int64_t* topk_idx,
+                 const float* topk_w, int payload, int32_t* counts, int32_t* offsets,
+                 int32_t* pool_src, int32_t* slot_to_pool, float* pool_w, void* pool,
+                 uint8_t* pool_scales, void* workspace, size_t workspace_bytes,
+                 moe_stream_t stream);
+
+/*
+ * Combine only: y[t] = bf16( sum over k = 0..K-1 with slot_to_pool[t*K+k] >= 0
+ * of [topk_w[t*K+k] *] fp32(pool_out[slot_to_pool[t*K+k]]) ), fp32 adds in
+ * ascending k starting from +0.  [P1] "combine_utils.cuh" snippet; [P3]
+ * section 5.1.  topk_w may be NULL (unweighted: the fused layer applies the
+ * weight before L2); with weights each product is rounded to fp32 before
+ * the add.
+ *   pool_out      bf16 [R][H] in pool order (R = rows referenced)
+ *   slot_to_pool  int32 [T*K]
+ *   y             bf16 [T][H]
+ * Shapes: H % 8 == 0.
+ */
+int moe_combine(const moe_shape_t* s, const void* pool_out, const int32_t* slot_to_pool,
+                const float* topk_w, void* y, moe_stream_t stream);
+
+/* Byte offsets of intermediates inside a moe_fused_forward workspace, so that
+ * tests can read them after a call (all -1 on a bad shape). */
+typedef struct {
+    int64_t counts, offsets, pool_src, slot_to_pool, pool_w; /* routing arrays */
+    int64_t pool_q, pool_s;   /* e4m3 [cap][H], ue8m0 [cap][H/32] */
+    int64_t act_q, act_s;     /* e4m3 [cap][I], ue8m0 [cap][I/32] */
+    int64_t l2_out;           /* bf16 [cap][H] */
+    int64_t capacity_rows;    /* cap = T*K + tile padding */
+} moe_workspace_views_t;
+
+int moe_workspace_views(const moe_shape_t* s, moe_workspace_views_t* v);
+
+/* Human-readable text of a status code (static storage). */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

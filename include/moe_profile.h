@@ -1,0 +1,47 @@
+/*
+ * moe_profile.h -- per-kernel timing of moe_fused_forward, for benchmarks.
+ *
+ * While profiling is on, every moe_fused_forward call records a HIP event on
+ * its stream before its first launch and after each of its launches, so the
+ * time between two consecutive events is one kernel's duration on the GPU
+ * (plus the launch gap).  Nothing is synchronised until moe_profile_stop.
+ * Calls beyond max_calls are not recorded.  Not thread-safe: profile one
+ * caller at a time.
+ */
+#ifndef MOE_PROFILE_H
+#define MOE_PROFILE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Stages of moe_fused_forward, in launch order. */
+enum {
+    MOE_STAGE_ROUTE_COUNT = 0, /* a1: per-segment expert histogram */
+    MOE_STAGE_ROUTE_SCAN,      /* a2: offsets, segment bases, m-tile table */
+    MOE_STAGE_ROUTE_SCATTER,   /* a3: stable rank -> pool_src, slot_to_pool, pool_w */
+    MOE_STAGE_DISPATCH,        /* a4: gather + e4m3 quantisation into the pool */
+    MOE_STAGE_GEMM_L1,         /* a5-a7: L1 GEMM, SwiGLU*w, e4m3 requant */
+    MOE_STAGE_GEMM_L2,         /* a8: L2 GEMM, bf16 rows */
+    MOE_STAGE_COMBINE,         /* a9: top-k fp32 reduction to bf16 */
+    MOE_PROFILE_STAGES
+};
+
+/* Start recording (creates 8 events per call slot; host allocation only).
+ * Returns 0, or MOE_ERR_INVALID_ARG for max_calls outside 1..4096, or
+ * MOE_ERR_DEVICE if the events cannot be created. */
+int moe_profile_start(int max_calls);
+
+/* Stop, wait for the recorded events, and write the summed milliseconds of
+ * each stage into stage_ms[MOE_PROFILE_STAGES] and the number of recorded
+ * calls into *ncalls.  Returns 0, or MOE_ERR_INVALID_ARG if profiling was not
+ * started, or MOE_ERR_DEVICE on an event error. */
+int moe_profile_stop(double* stage_ms, int* ncalls);
+
+/* Short name of a stage ("gemm_l1", ...), or "?" . */
+const char* moe_profile_stage_name(int stage);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

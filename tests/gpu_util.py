@@ -1,0 +1,78 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, call the C ABI
+through the thin binding, read intermediates back out of the workspace."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import combine_dispatch_amd as moe
+
+DEV = "cuda:0"
+
+
+def to_dev(inp: dict) -> dict:
+    d = {}
+    for k in ("x", "topk_idx", "topk_w", "W1q", "S1", "W2q", "S2"):
+        if k not in inp:
+            continue
+        a = np.ascontiguousarray(inp[k])
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        d[k] = torch.from_numpy(a).to(DEV)
+    return d
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def run_forward(inp: dict, dev: dict | None = None, opts=None, workspace=None):
+    """Returns (y bits [T][H], workspace tensor)."""
+    dev = dev or to_dev(inp)
+    T, H, I, E, K = (inp[k] for k in ("T", "H", "I", "E", "K"))
+    if workspace is None:
+        workspace = torch.empty(moe.moe_workspace_bytes(T, H, I, E, K), dtype=torch.uint8, device=DEV)
+    y = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    moe.moe_fused_forward(dev["x"], dev["topk_idx"], dev["topk_w"], dev["W1q"], dev["S1"],
+                          dev["W2q"], dev["S2"], y, workspace, opts=opts, E=E, I=I)
+    torch.cuda.synchronize()
+    return bf16_bits(y), workspace
+
+
+def view(workspace: torch.Tensor, inp: dict, name: str, rows: int | None = None) -> np.ndarray:
+    """Read an intermediate of a fused forward out of its workspace."""
+    T, H, I, E, K = (inp[k] for k in ("T", "H", "I", "E", "K"))
+    v = moe.moe_workspace_views(T, H, I, E, K)
+    TK = T * K
+    spec = {
+        "counts": (np.int32, (E,)), "offsets": (np.int32, (E + 1,)),
+        "pool_src": (np.int32, (TK,)), "slot_to_pool": (np.int32, (TK,)),
+        "pool_w": (np.float32, (TK,)), "pool_q": (np.uint8, (TK, H)),
+        "pool_s": (np.uint8, (TK, H // 32)), "act_q": (np.uint8, (TK, I)),
+        "act_s": (np.uint8, (TK, I // 32)), "l2_out": (np.uint16, (TK, H)),
+    }
+    dt, shape = spec[name]
+    if rows is not None:
+        shape = (rows,) + shape[1:]
+    nbytes = int(np.prod(shape)) * np.dtype(dt).itemsize
+    off = v[name]
+    return workspace[off:off + nbytes].cpu().numpy().view(dt).reshape(shape)
+
+
+def rel_l2_rows(y: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-row relative L2 error of bf16 bit arrays."""
+    yf = (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    rf = (ref.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    num = np.linalg.norm(yf - rf, axis=1)
+    den = np.linalg.norm(rf, axis=1)
+    return np.where(den > 0, num / np.maximum(den, 1e-300), num)
+
+
+def e4m3_step_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """|index difference| of two e4m3 codes on the ordered value line
+    (sign-magnitude codes mapped to a monotone integer scale)."""
+    def ordinal(c):
+        c = c.astype(np.int32)
+        mag = c & 0x7F
+        return np.where(c & 0x80, -mag, mag)
+    return np.abs(ordinal(a) - ordinal(b))

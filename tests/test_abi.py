@@ -1,0 +1,101 @@
+"""CPU-only checks of the C ABI library: it loads, exports every symbol that
+include/moe.h declares, and its host-side logic (shape checks, workspace
+sizing, status strings, argument errors found before any launch) behaves."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^\s*[\w\s\*]+?\b(moe_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import combine_dispatch_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from combine_dispatch_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("moe_fused_forward", "moe_dispatch", "moe_combine", "moe_workspace_bytes",
+              "moe_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(moe):
+    L = moe.lib()
+    for n in _declared_functions():
+        assert hasattr(L, n), n
+    assert set(moe.EXPORTED) <= set(_declared_functions())
+
+
+def test_status_strings(moe):
+    for st in (0, -1, -2, -3, -4, -5, 17):
+        assert isinstance(moe.moe_status_string(st), str) and moe.moe_status_string(st)
+
+
+def test_default_options(moe):
+    o = moe.moe_default_options()
+    assert o.fast_math == 1 and o.debug_validate == 0 and o.activation_clamp != o.activation_clamp
+
+
+def test_workspace_sizing(moe):
+    T, H, I, E, K = 8192, 7168, 2048, 32, 8
+    b = moe.moe_workspace_bytes(T, H, I, E, K)
+    cap = T * K + 256
+    # pool e4m3 + scales, act e4m3 + scales, L2 bf16 rows: the bulk of it
+    bulk = cap * (H + H // 32 + I + I // 32 + 2 * H)
+    assert bulk <= b <= bulk + 64 * 1024 * 1024
+    v = moe.moe_workspace_views(T, H, I, E, K)
+    assert v["capacity_rows"] == cap
+    offs = sorted(v[k] for k in v if k != "capacity_rows")
+    assert len(set(offs)) == len(offs) and all(o % 256 == 0 for o in offs)
+    assert v["l2_out"] + 2 * H * cap <= b
+    assert moe.moe_workspace_bytes(-1, H, I, E, K) == 0
+    assert moe.moe_workspace_bytes(T, H, I, 0, K) == 0
+    assert moe.moe_workspace_bytes(T, H, I, 2000, K) == 0
+    assert moe.moe_workspace_bytes(T, H, I, E, 65) == 0
+    assert 0 < moe.moe_dispatch_workspace_bytes(T, H, E, K) < b
+
+
+def test_host_side_errors_need_no_device(moe):
+    L = moe.lib()
+    s = moe.MoeShape(16, 256, 128, 4, 2)
+    null = ctypes.c_void_p(0)
+    # T == 0 returns at once, nothing to launch
+    assert L.moe_fused_forward(ctypes.byref(moe.MoeShape(0, 256, 128, 4, 2)), None, *[null] * 8,
+                               null, 0, null) == moe.MOE_OK
+    # null tensors -> invalid argument, found before any launch
+    assert L.moe_fused_forward(ctypes.byref(s), None, *[null] * 8, null, 0,
+                               null) == moe.MOE_ERR_INVALID_ARG
+    # shape outside the tiling
+    bad = moe.MoeShape(16, 200, 128, 4, 2)
+    assert L.moe_fused_forward(ctypes.byref(bad), None, *[null] * 8, null, 0,
+                               null) == moe.MOE_ERR_UNSUPPORTED
+    # activation clamp is not implemented
+    o = moe.options(activation_clamp=3.0)
+    assert L.moe_fused_forward(ctypes.byref(s), ctypes.byref(o), *[null] * 8, null, 0,
+                               null) == moe.MOE_ERR_UNSUPPORTED
+    # unknown payload
+    assert L.moe_dispatch(ctypes.byref(s), null, null, null, 7, *[null] * 7, null, 0,
+                          null) == moe.MOE_ERR_INVALID_ARG
+    # combine with T == 0 is a no-op, with nulls an error
+    assert L.moe_combine(ctypes.byref(moe.MoeShape(0, 256, 32, 1, 2)), null, null, null, null,
+                         null) == moe.MOE_OK
+    assert L.moe_combine(ctypes.byref(s), null, null, null, null, null) == moe.MOE_ERR_INVALID_ARG

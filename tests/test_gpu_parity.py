@@ -1,0 +1,276 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.
+
+Bars (routing and dispatch are integer/byte work, the rest floating point):
+  - counts, offsets, pool_src, slot_to_pool, pool_w, pool codes and pool
+    scale bytes: bit-exact;
+  - combine fed identical bf16 rows: bit-exact (same summation order);
+  - intermediate FP8 activations after L1: scale bytes and codes identical
+    except at most 0.1% of elements, which may be one code step apart (one
+    scale step for scale bytes);
+  - y: per-token relative L2 error <= 2e-2, all-masked tokens exactly +0.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+import oracle
+from tests.gpu_util import (DEV, bf16_bits, e4m3_step_distance, rel_l2_rows, run_forward, to_dev,
+                            view)
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL = 2e-2
+CODE_FRAC = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import combine_dispatch_amd as moe
+    moe.lib()  # fails loudly if the HIP library is missing
+
+
+def check_routing(inp, ws):
+    r = oracle.route(inp["topk_idx"], inp["topk_w"], inp["E"])
+    R = int(r["offsets"][-1])
+    np.testing.assert_array_equal(view(ws, inp, "counts"), r["counts"])
+    np.testing.assert_array_equal(view(ws, inp, "offsets"), r["offsets"])
+    np.testing.assert_array_equal(view(ws, inp, "pool_src")[:R], r["pool_src"][:R])
+    np.testing.assert_array_equal(view(ws, inp, "slot_to_pool"), r["slot_to_pool"])
+    np.testing.assert_array_equal(view(ws, inp, "pool_w")[:R].view(np.uint32),
+                                  r["pool_w"][:R].view(np.uint32))
+    return r, R
+
+
+def check_act(gq, gs, rq, rs):
+    """FP8 intermediate: codes [n][I], scale bytes [n][I/32]."""
+    sdiff = np.abs(gs.astype(np.int32) - rs.astype(np.int32))
+    assert sdiff.max(initial=0) <= 1
+    assert (sdiff != 0).mean() <= CODE_FRAC
+    same = np.repeat(sdiff == 0, 32, axis=1)
+    dist = e4m3_step_distance(gq, rq)
+    assert dist[same].max(initial=0) <= 1
+    assert (dist[same] != 0).mean() <= CODE_FRAC, (dist[same] != 0).mean()
+    if (~same).any():  # scale moved by one step: values within one step of the coarser scale
+        gv = oracle.e4m3_to_f32(gq) * np.exp2(np.repeat(gs, 32, axis=1).astype(np.float64) - 127)
+        rv = oracle.e4m3_to_f32(rq) * np.exp2(np.repeat(rs, 32, axis=1).astype(np.float64) - 127)
+        coarse = np.exp2(np.maximum(np.repeat(gs, 32, 1), np.repeat(rs, 32, 1)).astype(np.float64) - 127)
+        assert (np.abs(gv - rv)[~same] <= 32 * coarse[~same]).all()
+
+
+def check_y(y, ref, idx):
+    rel = rel_l2_rows(y, ref)
+    masked = (idx < 0).all(axis=1)
+    assert (y[masked] == 0).all()
+    assert rel[~masked].max(initial=0) <= Y_TOL, rel.max()
+    return float(rel.max(initial=0))
+
+
+# ----------------------------------------------------------------------------
+# small shapes: every intermediate against the grouped oracle
+# ----------------------------------------------------------------------------
+SMALL = [
+    dict(name="tiny"),
+    # several M tiles, ragged tails, masked slots, skewed routing, K-steps 4
+    dict(T=300, H=512, I=256, E=6, K=3, routing="zipf", seed=41, mask_p=0.1),
+    # one expert, one slot: a dense FFN
+    dict(T=97, H=256, I=128, E=1, K=1, routing="uniform", seed=42),
+    # many experts, several empty, T not a multiple of anything
+    dict(T=71, H=768, I=384, E=40, K=4, routing="zipf", seed=43, zipf_s=2.0, mask_p=0.05),
+    # every slot of some tokens masked
+    dict(T=64, H=256, I=128, E=4, K=2, routing="uniform", seed=44, mask_p=0.6),
+]
+
+
+def small_inputs(case):
+    if "name" in case:
+        return moe_inputs.config_inputs(case["name"])
+    return moe_inputs.make_inputs(**case)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=["tiny", "ragged", "dense", "sparse", "masked"])
+def test_forward_matches_oracle_small(case):
+    inp = small_inputs(case)
+    say("case", case)
+    y_ref, mid = oracle.forward(inp, intermediates=True)
+    y, ws = run_forward(inp)
+    r, R = check_routing(inp, ws)
+    np.testing.assert_array_equal(view(ws, inp, "pool_q", R), mid["pool_q"][:R])
+    np.testing.assert_array_equal(view(ws, inp, "pool_s", R), mid["pool_s"][:R])
+    check_act(view(ws, inp, "act_q", R), view(ws, inp, "act_s", R), mid["act_q"][:R],
+              mid["act_s"][:R])
+    worst = check_y(y, y_ref, inp["topk_idx"])
+    say("max rel l2", worst, "exact y fraction", float((y == y_ref).mean()))
+
+
+def test_forward_is_deterministic():
+    inp = small_inputs(SMALL[1])
+    dev = to_dev(inp)
+    y1, ws1 = run_forward(inp, dev)
+    y2, ws2 = run_forward(inp, dev)
+    np.testing.assert_array_equal(y1, y2)
+    R = int(view(ws1, inp, "offsets")[-1])
+    for name in ("pool_src", "pool_q", "act_q", "act_s", "l2_out"):  # rows past R are scratch
+        np.testing.assert_array_equal(view(ws1, inp, name, R), view(ws2, inp, name, R))
+
+
+# ----------------------------------------------------------------------------
+# dispatch and combine entry points on their own
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("payload", [0, 1], ids=["fp8", "bf16"])
+def test_dispatch_entry_matches_oracle(payload):
+    import combine_dispatch_amd as moe
+    inp = moe_inputs.make_inputs(T=513, H=352, I=32, E=13, K=5, routing="zipf", seed=51,
+                                 mask_p=0.1, weights=False)
+    T, H, E, K = inp["T"], inp["H"], inp["E"], inp["K"]
+    ref = oracle.dispatch(inp["x"], inp["topk_idx"], inp["topk_w"], E, payload)
+    dev = to_dev(inp)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    counts, offsets = torch.empty(E, **i32), torch.empty(E + 1, **i32)
+    pool_src, s2p = torch.full((T * K,), -7, **i32), torch.empty(T * K, **i32)
+    pool_w = torch.empty(T * K, dtype=torch.float32, device=DEV)
+    pool = torch.empty((T * K, H), dtype=torch.uint8 if payload == 0 else torch.int16, device=DEV)
+    scales = torch.empty((T * K, H // 32), dtype=torch.uint8, device=DEV) if payload == 0 else None
+    ws = torch.empty(moe.moe_dispatch_workspace_bytes(T, H, E, K), dtype=torch.uint8, device=DEV)
+    moe.moe_dispatch(dev["x"], dev["topk_idx"], dev["topk_w"], E, payload, counts, offsets,
+                     pool_src, s2p, pool_w, pool, scales, ws)
+    torch.cuda.synchronize()
+    R = int(ref["offsets"][-1])
+    np.testing.assert_array_equal(counts.cpu().numpy(), ref["counts"])
+    np.testing.assert_array_equal(offsets.cpu().numpy(), ref["offsets"])
+    np.testing.assert_array_equal(pool_src.cpu().numpy()[:R], ref["pool_src"][:R])
+    np.testing.assert_array_equal(s2p.cpu().numpy(), ref["slot_to_pool"])
+    np.testing.assert_array_equal(pool_w.cpu().numpy()[:R], ref["pool_w"][:R])
+    got = pool.cpu().numpy()[:R]
+    if payload == 1:
+        got = got.view(np.uint16)
+    np.testing.assert_array_equal(got, ref["pool"][:R])
+    if payload == 0:
+        np.testing.assert_array_equal(scales.cpu().numpy()[:R], ref["pool_scales"][:R])
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_combine_entry_bit_exact(weighted):
+    import combine_dispatch_amd as moe
+    T, H, K = 777, 1024, 8
+    rng = np.random.default_rng(61)
+    R = T * K
+    o = (rng.standard_normal((R, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    s2p = rng.permutation(R).astype(np.int32)
+    s2p[rng.random(R) < 0.2] = -1
+    s2p[:K] = -1  # token 0 fully masked
+    w = rng.random((T, K)).astype(np.float32)
+    ref = oracle.combine(o, s2p, T, K, w if weighted else None)
+    y = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    moe.moe_combine(torch.from_numpy(o.view(np.int16)).to(DEV), torch.from_numpy(s2p).to(DEV), T,
+                    K, y, torch.from_numpy(w).to(DEV) if weighted else None)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_bits(y), ref)
+
+
+def test_dispatch_then_combine_identity_k1():
+    """K = 1, bf16 payload, no expert in between: combine returns x exactly."""
+    import combine_dispatch_amd as moe
+    inp = moe_inputs.make_inputs(T=1000, H=2048, I=32, E=16, K=1, routing="uniform", seed=62,
+                                 weights=False)
+    T, H, E, K = 1000, 2048, 16, 1
+    dev = to_dev(inp)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    counts, offsets = torch.empty(E, **i32), torch.empty(E + 1, **i32)
+    pool_src, s2p = torch.empty(T * K, **i32), torch.empty(T * K, **i32)
+    pool_w = torch.empty(T * K, dtype=torch.float32, device=DEV)
+    pool = torch.empty((T * K, H), dtype=torch.int16, device=DEV)
+    ws = torch.empty(moe.moe_dispatch_workspace_bytes(T, H, E, K), dtype=torch.uint8, device=DEV)
+    moe.moe_dispatch(dev["x"], dev["topk_idx"], dev["topk_w"], E, 1, counts, offsets, pool_src,
+                     s2p, pool_w, pool, None, ws)
+    y = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    moe.moe_combine(pool, s2p, T, K, y)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_bits(y), inp["x"])
+
+
+# ----------------------------------------------------------------------------
+# edge cases and error conventions
+# ----------------------------------------------------------------------------
+def test_edge_empty_and_all_masked():
+    inp = moe_inputs.make_inputs(T=0, H=256, I=128, E=4, K=2, routing="uniform", seed=1)
+    y, _ = run_forward(inp)
+    assert y.shape == (0, 256)
+    inp = moe_inputs.make_inputs(T=37, H=256, I=128, E=4, K=2, routing="uniform", seed=1,
+                                 mask_p=1.0)
+    y, ws = run_forward(inp)
+    assert (y == 0).all()
+    assert (view(ws, inp, "counts") == 0).all()
+
+
+def test_errors_are_reported():
+    import combine_dispatch_amd as moe
+    inp = moe_inputs.make_inputs(T=16, H=256, I=128, E=4, K=2, routing="uniform", seed=2)
+    bad = dict(inp)
+    bad["topk_idx"] = inp["topk_idx"].copy()
+    bad["topk_idx"][3, 1] = 4  # == E
+    with pytest.raises(moe.MoeError) as ei:
+        run_forward(bad, opts=moe.options(debug_validate=True))
+    assert ei.value.status == moe.MOE_ERR_BAD_ROUTING
+    # the same call without validation treats the slot as masked and does not fault
+    y, ws = run_forward(bad)
+    assert view(ws, bad, "slot_to_pool")[3 * 2 + 1] == -1
+    small = torch.empty(1024, dtype=torch.uint8, device=DEV)
+    with pytest.raises(moe.MoeError) as ei:
+        run_forward(inp, workspace=small)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+    with pytest.raises(moe.MoeError) as ei:
+        run_forward(inp, opts=moe.options(activation_clamp=7.0))
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    odd = moe_inputs.make_inputs(T=8, H=128, I=128, E=2, K=1, routing="uniform", seed=3)
+    with pytest.raises(moe.MoeError) as ei:
+        run_forward(odd)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_exact_math_option_also_within_tolerance():
+    import combine_dispatch_amd as moe
+    inp = small_inputs(SMALL[1])
+    y_ref = oracle.forward(inp)
+    y, _ = run_forward(inp, opts=moe.options(fast_math=False))
+    check_y(y, y_ref, inp["topk_idx"])
+
+
+# ----------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark times
+# ----------------------------------------------------------------------------
+FULL = ["small", "prefill", "skewed", "many"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(name):
+    say("generating", name)
+    inp = moe_inputs.config_inputs(name)
+    say("running", name, {k: inp[k] for k in "THIEK"})
+    y, ws = run_forward(inp)
+    r, R = check_routing(inp, ws)
+    say("routing bit-exact, R =", R)
+    # pool bytes of sampled rows against the oracle's quantisation of the token row
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([rng.integers(0, R, 256), [0, R - 1]]))
+    pq, ps = view(ws, inp, "pool_q", R)[rows], view(ws, inp, "pool_s", R)[rows]
+    K, H = inp["K"], inp["H"]
+    for i, rr in enumerate(rows):
+        t = r["pool_src"][rr] // K
+        q, s = oracle.quant_e4m3_row(oracle.bf16_to_f32(inp["x"][t]))
+        np.testing.assert_array_equal(pq[i], q)
+        np.testing.assert_array_equal(ps[i], s)
+    # y on sampled tokens (including any fully masked one) against brute force
+    masked = np.nonzero((inp["topk_idx"] < 0).all(axis=1))[0][:2]
+    toks = np.unique(np.concatenate([rng.integers(0, inp["T"], 6), [0, inp["T"] - 1], masked]))
+    ref = oracle.forward_tokens(inp, toks.astype(np.int32))
+    worst = check_y(y[toks], ref, inp["topk_idx"][toks])
+    say(name, "sampled tokens", len(toks), "max rel l2", worst)
