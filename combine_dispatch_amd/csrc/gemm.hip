@@ -15,9 +15,11 @@
 //  - v_mfma_scale_f32_32x32x64_f8f6f4 with A = e4m3 (format 0), B = e2m1
 //    (format 4), scales per lane; fp32 accumulators in AGPRs.
 //  - 256 x 256 tile per 4-wave workgroup, each wave 128 x 128 (4 x 4 MFMA
-//    tiles); K steps of 128; global -> VGPR prefetch two steps ahead,
-//    VGPR -> LDS double buffer, XOR-swizzled 16-byte chunks so that the MFMA
-//    fragment reads are bank-conflict free.
+//    tiles); K steps of 128 staged through three LDS stages by direct
+//    global->LDS loads issued two steps ahead; 16-byte chunks XOR-swizzled so
+//    that the 16 lanes of each ds_read_b128 phase hit distinct banks of the
+//    64-bank LDS (A rows of 128 B: chunk ^ (row/2)%8; B rows of 64 B:
+//    chunk ^ (row/4)%4).
 //  - Expert-major m-tile table built on the device by the routing scan: no
 //    host synchronisation; surplus workgroups exit at once.
 //  - Workgroup ids are remapped so that each XCD (own L2) works on a
@@ -70,17 +72,55 @@ __device__ __forceinline__ int tile_of_block(int bid, int nblk) {
     return xcd * per + min(xcd, rem) + j;
 }
 
-struct Frags {
+// MFMA operands of one 64-wide K sub-step for one wave: A fragments of its 4
+// row tiles, B fragments of its 4 column tiles, per-lane scale registers.
+struct SubFrags {
     v8i a[4];
-    v8i b[4];
+    v4i b[4];
     int sa[4];
     int sb[4];
 };
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
+// Direct global -> LDS loads (global_load_lds_dwordx4 / _dword): lane l's
+// data lands at LDS address m0 + 16 l (4 l).  Written as inline asm so that
+// the compiler neither reorders LDS reads around them nor inserts its own
+// conservative vmcnt waits; the main loop counts them itself.  M0 is set
+// here; no compiler-generated code in these kernels reads M0.
+__device__ __forceinline__ void dma_x4(uint32_t lds, const void* sbase, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
+}
+__device__ __forceinline__ void dma_x1(uint32_t lds, const void* sbase, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
+}
+// Wait for this wave's direct loads except the newest 14 (or all), then a
+// workgroup barrier.  No memory fence: the data already sits in LDS.
+__device__ __forceinline__ void barrier_after_vmcnt14() {
+    asm volatile("s_waitcnt vmcnt(14) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void barrier_after_vmcnt28() {
+    asm volatile("s_waitcnt vmcnt(28) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void barrier_after_vmcnt0() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One LDS stage: A tile [256 rows][128 B], B tile [256 rows][64 B], then one
+// dword of scale bytes per A row and per B row.
 template <int MODE>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* smem) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8_t* st1,
+                                          uint8_t* st2, float* s_w) {
     const int tid = threadIdx.x;
-    const int wid = tid / 64, lane = tid % 64;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int lane = tid & 63;
     const int wm = wid >> 1, wn = wid & 1;
     const int h = lane >> 5, l32 = lane & 31;
 
@@ -92,69 +132,57 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* smem) {
     const int Kdim = g.Kdim;
     const int nk = Kdim / kBK;
 
-    float* s_w = reinterpret_cast<float*>(smem + kStages * kStageBytes);
     if (MODE == kL1) s_w[tid] = tid < nrows ? g.pool_w[row0 + tid] : 0.f;
 
-    // ---- global -> register staging addresses (constant per thread) -------
-    // A: 2048 16-byte chunks per step; chunk q = tid + 256 i covers LDS row
-    // q/8, physical chunk q%8, holding logical chunk (q%8) ^ (row%8).
-    const int a_row = tid >> 3;                     // + 32 i
-    const int a_chunk = (tid & 7) ^ ((tid >> 3) & 7);
-    const uint8_t* a_src = g.A + (int64_t)(row0 + a_row) * Kdim + 16 * a_chunk;
-    const int64_t a_stride32 = (int64_t)32 * Kdim;
-    // B: 1024 chunks; chunk q = tid + 256 i covers LDS row q/4, physical
-    // chunk q%4, logical chunk (q%4) ^ ((row/2)%4).
-    const int b_chunk = (tid & 3) ^ ((tid >> 3) & 3);
-    const int64_t b_ld = Kdim / 2;
-    const uint8_t* b_exp = g.B + (int64_t)e * g.N * b_ld + 16 * b_chunk;
-    const uint8_t* b_src0 = b_exp + b_row<MODE>(nt, (tid >> 2), g.I) * b_ld;
-    const uint8_t* b_src1 = b_exp + b_row<MODE>(nt, (tid >> 2) + 64, g.I) * b_ld;
-    const uint8_t* b_src2 = b_exp + b_row<MODE>(nt, (tid >> 2) + 128, g.I) * b_ld;
-    const uint8_t* b_src3 = b_exp + b_row<MODE>(nt, (tid >> 2) + 192, g.I) * b_ld;
-    // scales: one dword (4 k-blocks) per row per step
-    const uint8_t* sa_src = g.SA + (int64_t)(row0 + tid) * (Kdim / 32);
-    const uint8_t* sb_src = g.SB + ((int64_t)e * g.N + b_row<MODE>(nt, tid, g.I)) * (Kdim / 32);
+    // ---- global -> LDS direct loads --------------------------------------
+    // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS at M0 + 16 l,
+    // so one wave instruction fills 1 KiB of LDS; the lane's global address
+    // chooses which chunk lands there.  Addresses are a wave-uniform SGPR base
+    // (advanced by k each step) plus a per-lane 32-bit offset.
+    //
+    // A: 2048 16-byte chunks per step.  Chunk q = tid + 256 i (i = 0..7) is LDS
+    // row q/8, physical chunk q%8, holding logical chunk (q%8) ^ ((row/2)%8).
+    const int a_chunk = (tid & 7) ^ ((tid >> 4) & 7);
+    const uint32_t a_off = (uint32_t)((tid >> 3) * Kdim + 16 * a_chunk);
+    const uint32_t a_step32 = (uint32_t)(32 * Kdim);  // 32 rows = next i
+    const uint8_t* a_base = g.A + (int64_t)row0 * Kdim;
+    // B: 1024 chunks; chunk q = tid + 256 i is LDS row q/4 (B row b_row(q/4)),
+    // physical chunk q%4, logical chunk (q%4) ^ ((row/4)%4).
+    const int b_chunk = (tid & 3) ^ ((tid >> 4) & 3);
+    const int b_ld = Kdim / 2;
+    const uint8_t* b_base = g.B + ((int64_t)e * g.N + b_row<MODE>(nt, 0, g.I)) * b_ld;
+    const int b_r0 = b_row<MODE>(nt, 0, g.I);
+    const uint32_t b_off0 = (uint32_t)((b_row<MODE>(nt, (tid >> 2), g.I) - b_r0) * b_ld + 16 * b_chunk);
+    const uint32_t b_off1 = (uint32_t)((b_row<MODE>(nt, (tid >> 2) + 64, g.I) - b_r0) * b_ld + 16 * b_chunk);
+    const uint32_t b_off2 = (uint32_t)((b_row<MODE>(nt, (tid >> 2) + 128, g.I) - b_r0) * b_ld + 16 * b_chunk);
+    const uint32_t b_off3 = (uint32_t)((b_row<MODE>(nt, (tid >> 2) + 192, g.I) - b_r0) * b_ld + 16 * b_chunk);
+    // scales: one dword (4 k-blocks) per row per step; lane l of wave w is row 64 w + l
+    const int s_ld = Kdim / 32;
+    const uint8_t* sa_base = g.SA + (int64_t)row0 * s_ld;
+    const uint32_t sa_off = (uint32_t)(tid * s_ld);
+    const uint8_t* sb_base = g.SB + ((int64_t)e * g.N + b_r0) * s_ld;
+    const uint32_t sb_off = (uint32_t)((b_row<MODE>(nt, tid, g.I) - b_r0) * s_ld);
+    const uint32_t lds_st0 = lds_addr(st0), lds_st1 = lds_addr(st1), lds_st2 = lds_addr(st2);
+    const uint32_t w_dst16 = (uint32_t)(64 * wid * 16);
+    const uint32_t w_dst4 = (uint32_t)(64 * wid * 4);
 
-    // Staging registers as named scalars (arrays of them would be moved to
-    // LDS by the compiler's alloca promotion).
-    uint4 ra0, ra1, ra2, ra3, ra4, ra5, ra6, ra7, rb0, rb1, rb2, rb3;
-    uint32_t rsa, rsb;
-    auto load_global = [&](int kk) __attribute__((always_inline)) {
-        const int k0 = kk * kBK;
-        const uint8_t* pa = a_src + k0;
-        ra0 = *reinterpret_cast<const uint4*>(pa);
-        ra1 = *reinterpret_cast<const uint4*>(pa + a_stride32);
-        ra2 = *reinterpret_cast<const uint4*>(pa + 2 * a_stride32);
-        ra3 = *reinterpret_cast<const uint4*>(pa + 3 * a_stride32);
-        ra4 = *reinterpret_cast<const uint4*>(pa + 4 * a_stride32);
-        ra5 = *reinterpret_cast<const uint4*>(pa + 5 * a_stride32);
-        ra6 = *reinterpret_cast<const uint4*>(pa + 6 * a_stride32);
-        ra7 = *reinterpret_cast<const uint4*>(pa + 7 * a_stride32);
-        rb0 = *reinterpret_cast<const uint4*>(b_src0 + k0 / 2);
-        rb1 = *reinterpret_cast<const uint4*>(b_src1 + k0 / 2);
-        rb2 = *reinterpret_cast<const uint4*>(b_src2 + k0 / 2);
-        rb3 = *reinterpret_cast<const uint4*>(b_src3 + k0 / 2);
-        rsa = *reinterpret_cast<const uint32_t*>(sa_src + k0 / 32);
-        rsb = *reinterpret_cast<const uint32_t*>(sb_src + k0 / 32);
+    // 14 loads per wave per step (8 A, 4 B, 2 scale dwords); piece g (0..15)
+    // issues load g, pieces 14 and 15 issue nothing.
+    auto issue_piece = [&](uint32_t st, int k0, int g) __attribute__((always_inline)) {
+        if (g < 8) {
+            dma_x4(st + w_dst16 + 4096 * g, a_base + k0, a_off + g * a_step32);
+        } else if (g < 12) {
+            const uint32_t off = g == 8 ? b_off0 : g == 9 ? b_off1 : g == 10 ? b_off2 : b_off3;
+            dma_x4(st + kStageA + w_dst16 + 4096 * (g - 8), b_base + k0 / 2, off);
+        } else if (g == 12) {
+            dma_x1(st + kStageA + kStageB + w_dst4, sa_base + k0 / 32, sa_off);
+        } else if (g == 13) {
+            dma_x1(st + kStageA + kStageB + kStageSA + w_dst4, sb_base + k0 / 32, sb_off);
+        }
     };
-    auto store_lds = [&](int st) __attribute__((always_inline)) {
-        uint4* pa = reinterpret_cast<uint4*>(smem + st * kStageBytes) + tid;
-        pa[0] = ra0;
-        pa[256] = ra1;
-        pa[512] = ra2;
-        pa[768] = ra3;
-        pa[1024] = ra4;
-        pa[1280] = ra5;
-        pa[1536] = ra6;
-        pa[1792] = ra7;
-        uint4* pb = reinterpret_cast<uint4*>(smem + st * kStageBytes + kStageA) + tid;
-        pb[0] = rb0;
-        pb[256] = rb1;
-        pb[512] = rb2;
-        pb[768] = rb3;
-        uint32_t* ps = reinterpret_cast<uint32_t*>(smem + st * kStageBytes + kStageA + kStageB) + tid;
-        ps[0] = rsa;
-        ps[kStageSA / 4] = rsb;
+    auto issue = [&](uint32_t st, int kk) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < 14; ++g) issue_piece(st, kk * kBK, g);
     };
 
     v16f acc[4][4];
@@ -165,66 +193,125 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* smem) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // ---- fragment read addresses (LDS byte offsets inside a stage) ---------
-    // A row of row-tile i: 128*wm + 32*i + l32; row%8 == lane%8.
+    // ---- fragment reads --------------------------------------------------
+    // A row of row-tile i: 128*wm + 32*i + l32, so (row/2)%8 == (l32/2)%8.
     const int a_frag_row = 128 * wm + l32;
-    const int a_sw = lane & 7;
-    // B row of column tile j: wave_b_row0(j) + l32; (row/2)%4 == (l32/2)%4.
-    const int b_sw = (l32 >> 1) & 3;
+    const int a_sw = (l32 >> 1) & 7;
+    // B row of column tile j: wave_b_row0(j) + l32, so (row/4)%4 == (l32/4)%4.
+    const int b_sw = (l32 >> 2) & 3;
 
-    auto compute = [&](int st) __attribute__((always_inline)) {
-        const uint8_t* base = smem + st * kStageBytes;
+    // Operand reads of sub-step s (0 or 1) of the step held in an LDS stage,
+    // split into the pieces read next to each MFMA: scale bytes (each lane
+    // reads the byte of its k-block, so no shifts are needed), then B, then
+    // A -- the order in which the next sub-step's MFMAs consume them.
+    auto read_piece = [&](SubFrags& f, const uint8_t* base, int s, int g) __attribute__((always_inline)) {
         const uint8_t* sA = base;
         const uint8_t* sB = base + kStageA;
-        const uint32_t* sSA = reinterpret_cast<const uint32_t*>(base + kStageA + kStageB);
-        const uint32_t* sSB = reinterpret_cast<const uint32_t*>(base + kStageA + kStageB + kStageSA);
-        uint32_t wa[4], wb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) wa[i] = sSA[a_frag_row + 32 * i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wb[j] = sSB[wave_b_row0<MODE>(wn, j) + l32];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            Frags f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint8_t* rowp = sA + (a_frag_row + 32 * i) * kBK;
-                const uint4 lo = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * s + h) ^ a_sw));
-                const uint4 hi = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * s + 2 + h) ^ a_sw));
-                f.a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                f.sa[i] = (int)(wa[i] >> (8 * (2 * s + h)));
+        const uint8_t* sSA = base + kStageA + kStageB;
+        const uint8_t* sSB = sSA + kStageSA;
+        const int blk = 2 * s + h;
+        if (g < 4) {
+            f.sa[g] = sSA[(a_frag_row + 32 * g) * 4 + blk];
+            f.sb[g] = sSB[(wave_b_row0<MODE>(wn, g) + l32) * 4 + blk];
+            const uint8_t* rowp = sB + (wave_b_row0<MODE>(wn, g) + l32) * (kBK / 2);
+            const uint4 v = *reinterpret_cast<const uint4*>(rowp + 16 * ((2 * s + h) ^ b_sw));
+            f.b[g] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+        } else if (g < 12) {
+            const int i = (g - 4) >> 1, part = (g - 4) & 1;
+            const uint8_t* rowp = sA + (a_frag_row + 32 * i) * kBK;
+            const uint4 v = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * s + 2 * part + h) ^ a_sw));
+            if (part == 0) {
+                f.a[i][0] = (int)v.x; f.a[i][1] = (int)v.y; f.a[i][2] = (int)v.z; f.a[i][3] = (int)v.w;
+            } else {
+                f.a[i][4] = (int)v.x; f.a[i][5] = (int)v.y; f.a[i][6] = (int)v.z; f.a[i][7] = (int)v.w;
             }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint8_t* rowp = sB + (wave_b_row0<MODE>(wn, j) + l32) * (kBK / 2);
-                const uint4 v = *reinterpret_cast<const uint4*>(rowp + 16 * ((2 * s + h) ^ b_sw));
-                f.b[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-                f.sb[j] = (int)(wb[j] >> (8 * (2 * s + h)));
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        f.a[i], f.b[j], acc[i][j], 0, 4, 0, f.sa[i], 0, f.sb[j]);
         }
     };
+    auto read_all = [&](SubFrags& f, const uint8_t* base, int s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < 12; ++g) read_piece(f, base, s, g);
+    };
+    // MFMA number g (0..15) of a sub-step: row tile g/4, column tile g%4.
+    auto mfma_one = [&](const SubFrags& f, int g) __attribute__((always_inline)) {
+        const int i = g >> 2, j = g & 3;
+        const v8i b = v8i{f.b[j][0], f.b[j][1], f.b[j][2], f.b[j][3], 0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], b, acc[i][j], 0, 4, 0,
+                                                                     f.sa[i], 0, f.sb[j]);
+    };
 
-    // ---- main loop: prefetch two steps ahead, two LDS stages ---------------
-    load_global(0);
-    store_lds(0);
-    if (nk > 1) load_global(1);
-    __syncthreads();
-    for (int kk = 0; kk < nk; ++kk) {
-        if (kk + 1 < nk) store_lds((kk + 1) & 1);
-        if (kk + 2 < nk) load_global(kk + 2);
-        compute(kk & 1);
-        __syncthreads();
+    // ---- main loop: three LDS stages, sub-step pipelined operands ---------
+    // X holds sub-step 0 and Y sub-step 1 of the current step k.  While the 16
+    // MFMAs of X run, Y is read from step k's stage.  Then each wave waits
+    // for its own loads of step k+1 (all LDS reads of step k are done) and
+    // meets the others at a barrier: step k+1's stage is complete and step
+    // k's stage is free, so it is refilled with step k+3 -- those 14 loads
+    // are spread over the MFMAs of Y, while X is read from step k+1's stage.
+    // Every MFMA is fenced together with the reads/loads issued beside it, so
+    // the compiler keeps this order; the loop bodies are branch-free, and the
+    // last three steps run in a second loop that issues no loads and waits
+    // for all of them.
+    issue(lds_st0, 0);
+    if (nk > 1) issue(lds_st1, 1);
+    if (nk > 2) issue(lds_st2, 2);
+    if (nk > 2)
+        barrier_after_vmcnt28();
+    else if (nk > 1)
+        barrier_after_vmcnt14();
+    else
+        barrier_after_vmcnt0();
+    SubFrags X, Y;
+    read_all(X, st0, 0);
+    const uint8_t* cur = st0;
+    const uint8_t* next = st1;
+    const uint8_t* third = st2;
+    int k = 0;
+    for (; k + 3 < nk; ++k) {
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            mfma_one(X, g);
+            read_piece(Y, cur, 1, g);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        barrier_after_vmcnt14();
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t dst = lds_addr(cur);
+        const int k0 = (k + 3) * kBK;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            mfma_one(Y, g);
+            read_piece(X, next, 0, g);
+            issue_piece(dst, k0, g);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const uint8_t* t = cur;
+        cur = next;
+        next = third;
+        third = t;
     }
+    for (; k < nk; ++k) {
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            mfma_one(X, g);
+            read_piece(Y, cur, 1, g);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        barrier_after_vmcnt0();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            mfma_one(Y, g);
+            read_piece(X, next, 0, g);  // on the last step this reads a stale stage, unused
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const uint8_t* t = cur;
+        cur = next;
+        next = third;
+        third = t;
+    }
+    __syncthreads();  // stages are reused by the epilogue
 
     // ---- epilogue ------------------------------------------------------------
-    uint8_t* wbuf = smem + wid * 8192;  // per-wave staging, stages are free now
+    uint8_t* wbuf = st0 + wid * 8192;  // per-wave staging, stages are free now
     if (MODE == kL2) {
         const int N = g.N;
 #pragma unroll
@@ -297,13 +384,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* smem) {
 }  // namespace
 
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_l1(GemmArgs args) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kGemmLds];
-    gemm_tile<kL1>(args, smem);
+    __shared__ __attribute__((aligned(16))) uint8_t st0[kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[kStageBytes];
+    __shared__ float s_w[kBM];
+    gemm_tile<kL1>(args, st0, st1, st2, s_w);
 }
 
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_l2(GemmArgs args) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kGemmLds];
-    gemm_tile<kL2>(args, smem);
+    __shared__ __attribute__((aligned(16))) uint8_t st0[kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[kStageBytes];
+    __shared__ float s_w[kBM];
+    gemm_tile<kL2>(args, st0, st1, st2, s_w);
 }
 
 }  // namespace moe

@@ -61,20 +61,34 @@ __device__ __forceinline__ float unscale(float v, uint32_t b) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-// Max over the 4 lanes of an aligned quad (DPP quad permutes).
+// DPP lane permutations (gfx9 encodings of the dpp_ctrl field).
+constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7-i inside each 8 lanes
+constexpr int kDppRowMirror = 0x140;      // lane i <-> 15-i inside each 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over the 4 lanes of an aligned quad (all lanes get it).
 __device__ __forceinline__ float quad_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 1));
-    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, dpp<kDppQuadSwap1>(v));
+    v = fmaxf(v, dpp<kDppQuadSwap2>(v));
     return v;
 }
 
-// Max over the 32 lanes of each wave half.
+// Max over each aligned group of 32 lanes (all lanes get it): four DPP steps
+// reduce each row of 16 lanes, one ds_swizzle (lane ^ 16 inside 32) joins the
+// two rows.
 __device__ __forceinline__ float half_wave_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 1));
-    v = fmaxf(v, __shfl_xor(v, 2));
-    v = fmaxf(v, __shfl_xor(v, 4));
-    v = fmaxf(v, __shfl_xor(v, 8));
-    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, dpp<kDppQuadSwap1>(v));
+    v = fmaxf(v, dpp<kDppQuadSwap2>(v));
+    v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+    v = fmaxf(v, dpp<kDppRowMirror>(v));
+    // swizzle bitmask mode: and 0x1F, or 0, xor 0x10
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
     return v;
 }
 

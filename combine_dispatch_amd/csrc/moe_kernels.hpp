@@ -13,7 +13,8 @@ constexpr int kRouteWaves = 4;  // waves per routing block
 constexpr int kRouteThreads = kRouteWaves * 64;
 
 // Grouped GEMM tiling: 256 x 256 output tile per 256-thread workgroup,
-// 128 K per main-loop step, two LDS stages.
+// 128 K per main-loop step, three LDS stages filled by direct global->LDS
+// loads two steps ahead.
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kBK = 128;
@@ -23,8 +24,7 @@ constexpr int kStageB = kBN * kBK / 2;      // e2m1 bytes
 constexpr int kStageSA = kBM * 4;           // 4 scale bytes per row per step
 constexpr int kStageSB = kBN * 4;
 constexpr int kStageBytes = kStageA + kStageB + kStageSA + kStageSB;
-constexpr int kStages = 2;
-constexpr int kGemmLds = kStages * kStageBytes + kBM * 4;  // + routing weights
+constexpr int kStages = 3;
 
 struct MTile {
     int32_t expert, row0, nrows, pad;
