@@ -46,6 +46,7 @@ namespace {
 
 constexpr int kL1 = 0;
 constexpr int kL2 = 1;
+constexpr int kGroupM = 4;  // m-tiles per tile-order group
 
 // Which expert-matrix row (output column) holds LDS B row `nrow` of tile nt.
 template <int MODE>
@@ -124,9 +125,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     const int wm = wid >> 1, wn = wid & 1;
     const int h = lane >> 5, l32 = lane & 31;
 
+    // Tile order: groups of kGroupM m-tiles x all n-tiles, m fastest, so the
+    // ~32 workgroups an XCD runs at once cover 4 m-tiles x 8 n-tiles and
+    // share both operands through that XCD's L2.
     const int logical = tile_of_block(blockIdx.x, gridDim.x);
-    const int mt = logical / g.ntiles, nt = logical % g.ntiles;
-    if (mt >= *g.num_mtiles) return;
+    const int num_m = *g.num_mtiles;
+    if (logical >= num_m * g.ntiles) return;
+    const int group = logical / (kGroupM * g.ntiles);
+    const int in_group = logical - group * (kGroupM * g.ntiles);
+    const int gm = min(kGroupM, num_m - group * kGroupM);
+    const int mt = group * kGroupM + in_group % gm;
+    const int nt = in_group / gm;
     const MTile tile = g.mtiles[mt];
     const int e = tile.expert, row0 = tile.row0, nrows = tile.nrows;
     const int Kdim = g.Kdim;
@@ -308,45 +317,41 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
         next = third;
         third = t;
     }
-    __syncthreads();  // stages are reused by the epilogue
-
     // ---- epilogue ------------------------------------------------------------
-    uint8_t* wbuf = st0 + wid * 8192;  // per-wave staging, stages are free now
+    // Each lane holds column l32 of 16 rows per MFMA tile.  A 4x4 transpose
+    // inside every quad of lanes (two DPP exchanges and byte permutes) turns
+    // that into 4 consecutive columns of one row, stored straight to global
+    // memory: no LDS, 4-byte (codes) or 8-byte (bf16) stores.
+    const int q4 = lane & 3;   // position inside the quad
+    const int m4 = l32 >> 2;   // quad number: columns 4*m4 .. 4*m4+3 of a 32-column tile
     if (MODE == kL2) {
         const int N = g.N;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // bf16 tile of 32 rows x 128 columns, row-major, 256 B per row
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int rr = 8 * (r >> 2) + 4 * h + (r & 3);
-                    const float v = acc[i][j][r];
-                    reinterpret_cast<uint16_t*>(wbuf)[rr * 128 + 32 * j + l32] =
-                        (uint16_t)pack_bf16x2(v, 0.f);
+                for (int grp = 0; grp < 4; ++grp) {
+                    // rows 8*grp + 4*h + 0..3 of row tile i, column 32*j + l32
+                    uint32_t x0 = pack_bf16x2(acc[i][j][4 * grp + 0], acc[i][j][4 * grp + 1]);
+                    uint32_t x1 = pack_bf16x2(acc[i][j][4 * grp + 2], acc[i][j][4 * grp + 3]);
+                    quad_transpose_b16(x0, x1, q4);
+                    const int lrow = 128 * wm + 32 * i + 8 * grp + 4 * h + q4;
+                    if (lrow < nrows)
+                        *reinterpret_cast<uint2*>(g.out + (int64_t)(row0 + lrow) * N + nt * kBN +
+                                                  128 * wn + 32 * j + 4 * m4) = make_uint2(x0, x1);
                 }
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int q = lane + 64 * m;
-                const int rr = q >> 4, cu = q & 15;
-                const int lrow = 128 * wm + 32 * i + rr;
-                const uint4 v = reinterpret_cast<const uint4*>(wbuf)[q];
-                if (lrow < nrows)
-                    *reinterpret_cast<uint4*>(g.out + (int64_t)(row0 + lrow) * N + nt * kBN +
-                                              128 * wn + 8 * cu) = v;
-            }
-        }
     } else {
         const int I = g.I;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
+                uint32_t codes[16];
+                uint32_t my_scale = 0;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int rr = 8 * (r >> 2) + 4 * h + (r & 3);
-                    const int lrow = 128 * wm + 32 * i + rr;
                     const float gt = round_bf16(acc[i][jj][r]);
                     const float up = round_bf16(acc[i][jj + 2][r]);
                     float sl;
@@ -356,26 +361,26 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
                     } else {
                         sl = gt / (1.0f + expf(-gt));
                     }
-                    const float a = (sl * up) * s_w[lrow];
+                    const float a = (sl * up) * s_w[128 * wm + 32 * i + rr];
                     const float amax = half_wave_max(fabsf(a));
                     const uint32_t b = ue8m0_e4m3(amax);
-                    const uint32_t code = pack_fp8x2(unscale(a, b), 0.f) & 0xFFu;
-                    wbuf[rr * 64 + 32 * jj + l32] = (uint8_t)code;
-                    if (l32 == 0 && lrow < nrows)
-                        g.act_s[(int64_t)(row0 + lrow) * (I / 32) + (nt * 128 + 64 * wn) / 32 + jj] =
-                            (uint8_t)b;
+                    codes[r] = pack_fp8x2(unscale(a, b), 0.f) & 0xFFu;
+                    if (l32 == r) my_scale = b;  // lane r (< 16) stores the scale of row r
                 }
-            }
-            // 32 rows x 64 code bytes -> global, 16 bytes per lane
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int q = lane + 64 * m;
-                const int rr = q >> 2, cu = q & 3;
-                const int lrow = 128 * wm + 32 * i + rr;
-                const uint4 v = reinterpret_cast<const uint4*>(wbuf)[q];
-                if (lrow < nrows)
-                    *reinterpret_cast<uint4*>(g.act_q + (int64_t)(row0 + lrow) * I + nt * 128 +
-                                              64 * wn + 16 * cu) = v;
+                for (int grp = 0; grp < 4; ++grp) {
+                    uint32_t x = codes[4 * grp] | (codes[4 * grp + 1] << 8) |
+                                 (codes[4 * grp + 2] << 16) | (codes[4 * grp + 3] << 24);
+                    x = quad_transpose_b8(x, q4);
+                    const int lrow = 128 * wm + 32 * i + 8 * grp + 4 * h + q4;
+                    if (lrow < nrows)
+                        *reinterpret_cast<uint32_t*>(g.act_q + (int64_t)(row0 + lrow) * I + nt * 128 +
+                                                     64 * wn + 32 * jj + 4 * m4) = x;
+                }
+                const int srow = 128 * wm + 32 * i + 8 * (l32 >> 2) + 4 * h + (l32 & 3);
+                if (l32 < 16 && srow < nrows)
+                    g.act_s[(int64_t)(row0 + srow) * (I / 32) + (nt * 128 + 64 * wn) / 32 + jj] =
+                        (uint8_t)my_scale;
             }
         }
     }

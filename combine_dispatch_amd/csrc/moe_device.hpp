@@ -92,4 +92,29 @@ __device__ __forceinline__ float half_wave_max(float v) {
     return v;
 }
 
+// 4x4 transposes inside each quad of lanes.  Lane t of a quad holds element
+// (t, q) of a 4x4 block in part q of its register(s); afterwards it holds
+// element (q, t) in part q.  Two DPP exchanges (lane ^ 1, lane ^ 2) and
+// v_perm_b32 byte selects; t is the lane's position in its quad.
+__device__ __forceinline__ uint32_t quad_transpose_b8(uint32_t x, int t) {
+    const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kDppQuadSwap1, 0xF, 0xF, false);
+    const uint32_t r = __builtin_amdgcn_perm(y, x, (t & 1) ? 0x03070105u : 0x06020400u);
+    const uint32_t z = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, kDppQuadSwap2, 0xF, 0xF, false);
+    return __builtin_amdgcn_perm(z, r, (t & 2) ? 0x03020706u : 0x05040100u);
+}
+
+// Same for 16-bit elements: x0 = parts (0, 1), x1 = parts (2, 3).
+__device__ __forceinline__ void quad_transpose_b16(uint32_t& x0, uint32_t& x1, int t) {
+    // exchange 1: even lanes send their high halves, odd lanes their low halves
+    const uint32_t send = __builtin_amdgcn_perm(x1, x0, (t & 1) ? 0x05040100u : 0x07060302u);
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, kDppQuadSwap1, 0xF, 0xF, false);
+    const uint32_t n0 = __builtin_amdgcn_perm(recv, x0, (t & 1) ? 0x03020504u : 0x05040100u);
+    const uint32_t n1 = __builtin_amdgcn_perm(recv, x1, (t & 1) ? 0x03020706u : 0x07060100u);
+    // exchange 2: lanes 0,1 send n1, lanes 2,3 send n0
+    const uint32_t send2 = (t & 2) ? n0 : n1;
+    const uint32_t recv2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send2, kDppQuadSwap2, 0xF, 0xF, false);
+    x0 = (t & 2) ? recv2 : n0;
+    x1 = (t & 2) ? n1 : recv2;
+}
+
 }  // namespace moe
