@@ -21,6 +21,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -41,9 +42,44 @@ def parse():
                    help="tiny | small | prefill | skewed | many")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample (0 = skip)")
-    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                   help="measured HBM bytes per L1 launch (from rocprofv3 --pmc), if present")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="after the timed region, run one plain device-to-device copy of this "
+                        "many MiB (the known-size kernel that scales the HBM byte counters)")
     return p.parse_args()
+
+
+# HBM traffic of the L1 GEMM per launch, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, WRITE_SIZE) scaled by a plain copy of known size.  The summary
+# names the sha256 of the GEMM sources it was measured on; a changed kernel
+# reports null.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_l1_prefill_hbm_traffic.md")
+GEMM_SOURCES = ("combine_dispatch_amd/csrc/gemm.hip", "combine_dispatch_amd/csrc/moe_kernels.hpp",
+                "combine_dispatch_amd/csrc/moe_device.hpp")
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    if workload != "prefill" or not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_SUMMARY):
+        m = re.match(r"^\s*-?\s*`?([a-z0-9_]+)`?\s*:\s*`?([0-9a-f.]+)`?\s*$", line)
+        if m:
+            fields[m.group(1)] = m.group(2)
+    if fields.get("gemm_source_sha256") != gemm_source_hash():
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -90,9 +126,12 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` whole-layer steps
+    # timed region: exactly `steps` whole-layer steps.  The library records
+    # HIP events around each of its launches on the same stream, so the
+    # per-kernel durations come from this very region.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    moe.moe_profile_start(a.steps)
     wall0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(a.steps):
@@ -101,14 +140,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = ev0.elapsed_time(ev1) / a.steps
-
-    # per-kernel durations: HIP events recorded by the library on its stream
-    # around each launch, in a second pass of the same steps
-    moe.moe_profile_start(a.steps)
-    for _ in range(a.steps):
-        step()
     stage_ms, ncalls = moe.moe_profile_stop()
     per_launch = {k: v / max(ncalls, 1) for k, v in stage_ms.items()}
+
+    if a.copy_mib > 0:
+        n = a.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     flop = 6.0 * R * H * I
     tflops = flop / (ms_per_step * 1e-3) / 1e12
@@ -121,14 +163,7 @@ def main():
     disp_bytes = T * H * 2 + R * (H + H // 32) + T * K * 8 * 2
     comb_bytes = R * H * 2 + T * H * 2 + T * K * 4
 
-    traffic = None
-    if os.path.exists(a.traffic_json):
-        try:
-            tj = json.load(open(a.traffic_json))
-            if tj.get("workload") == a.workload and tj.get("kernel") == "gemm_l1":
-                traffic = tj.get("hbm_bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
+    traffic = measured_traffic(a.workload)
 
     out = {
         "metric": METRIC,

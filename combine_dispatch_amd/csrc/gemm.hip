@@ -49,20 +49,19 @@ constexpr int kL2 = 1;
 constexpr int kGroupM = 4;  // m-tiles per tile-order group
 
 // Which expert-matrix row (output column) holds LDS B row `nrow` of tile nt.
+// LDS B row n is column c = n%32 of MFMA column tile j = n/32.  The order is
+// chosen so that, after the MFMA, each lane holds adjacent output columns of a
+// row:
+//  L1: tiles 0-3 are gate, 4-7 the matching up columns; lane column c of tile
+//      j is activation column 4c + j%4 of the tile's 128, so a lane holds 4
+//      adjacent activation columns and the 8 lanes c = 8G..8G+7 hold the 32
+//      columns of quantisation group G.
+//  L2: lane column c of tile j is output column 8c + j of the tile's 256.
 template <int MODE>
 __device__ __forceinline__ int b_row(int nt, int nrow, int I) {
-    if (MODE == kL1) {
-        // rows 0..127: gate columns nt*128 + nrow; 128..255: the matching up columns
-        return nrow < 128 ? nt * 128 + nrow : I + nt * 128 + (nrow - 128);
-    }
-    return nt * kBN + nrow;
-}
-
-// LDS B row of this wave's column tile j (0..3).
-template <int MODE>
-__device__ __forceinline__ int wave_b_row0(int wn, int j) {
-    if (MODE == kL1) return (j < 2 ? 0 : 128) + 64 * wn + 32 * (j & 1);
-    return 128 * wn + 32 * j;
+    const int j = nrow >> 5, c = nrow & 31;
+    if (MODE == kL1) return (j < 4 ? 0 : I) + nt * 128 + 4 * c + (j & 3);
+    return nt * kBN + 8 * c + j;
 }
 
 __device__ __forceinline__ int tile_of_block(int bid, int nblk) {
@@ -73,13 +72,13 @@ __device__ __forceinline__ int tile_of_block(int bid, int nblk) {
     return xcd * per + min(xcd, rem) + j;
 }
 
-// MFMA operands of one 64-wide K sub-step for one wave: A fragments of its 4
-// row tiles, B fragments of its 4 column tiles, per-lane scale registers.
+// MFMA operands of one 64-wide K sub-step for one wave: A fragments of its 2
+// row tiles, B fragments of the 8 column tiles, per-lane scale registers.
 struct SubFrags {
-    v8i a[4];
-    v4i b[4];
-    int sa[4];
-    int sb[4];
+    v8i a[2];
+    v4i b[8];
+    int sa[2];
+    int sb[8];
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -94,13 +93,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // the compiler neither reorders LDS reads around them nor inserts its own
 // conservative vmcnt waits; the main loop counts them itself.  M0 is set
 // here; no compiler-generated code in these kernels reads M0.
+// The asm operands must sit in SGPRs; the values are wave-uniform by
+// construction and readfirstlane states that to the compiler (free when it
+// already knows).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void dma_x4(uint32_t lds, const void* sbase, uint32_t voff) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(sbase))
+                 : "memory");
 }
 __device__ __forceinline__ void dma_x1(uint32_t lds, const void* sbase, uint32_t voff) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-                 :: "s"(lds), "v"(voff), "s"(sbase) : "memory");
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(sbase))
+                 : "memory");
 }
 // Wait for this wave's direct loads except the newest 14 (or all), then a
 // workgroup barrier.  No memory fence: the data already sits in LDS.
@@ -122,7 +132,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     const int tid = threadIdx.x;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63;
-    const int wm = wid >> 1, wn = wid & 1;
+    const int wm = wid;  // rows 64*wm .. 64*wm+63 of the tile, all 256 columns
     const int h = lane >> 5, l32 = lane & 31;
 
     // Tile order: groups of kGroupM m-tiles x all n-tiles, m fastest, so the
@@ -194,39 +204,34 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
         for (int g = 0; g < 14; ++g) issue_piece(st, kk * kBK, g);
     };
 
-    v16f acc[4][4];
+    v16f acc[2][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // ---- fragment reads --------------------------------------------------
-    // A row of row-tile i: 128*wm + 32*i + l32, so (row/2)%8 == (l32/2)%8.
-    const int a_frag_row = 128 * wm + l32;
+    // A row of row-tile i: 64*wm + 32*i + l32, so (row/2)%8 == (l32/2)%8.
+    const int a_frag_row = 64 * wm + l32;
     const int a_sw = (l32 >> 1) & 7;
-    // B row of column tile j: wave_b_row0(j) + l32, so (row/4)%4 == (l32/4)%4.
+    // B row of column tile j: 32*j + l32, so (row/4)%4 == (l32/4)%4.
     const int b_sw = (l32 >> 2) & 3;
 
     // Operand reads of sub-step s (0 or 1) of the step held in an LDS stage,
-    // split into the pieces read next to each MFMA: scale bytes (each lane
-    // reads the byte of its k-block, so no shifts are needed), then B, then
-    // A -- the order in which the next sub-step's MFMAs consume them.
+    // split into the pieces read next to each MFMA, in the order the next
+    // sub-step's MFMAs (row tile 0 with column tiles 0..7, then row tile 1)
+    // consume them: A scales and row tile 0, then each column tile with its
+    // scale, then row tile 1.  Each lane reads the scale byte of its own
+    // k-block, so no shifts are needed.
     auto read_piece = [&](SubFrags& f, const uint8_t* base, int s, int g) __attribute__((always_inline)) {
         const uint8_t* sA = base;
         const uint8_t* sB = base + kStageA;
         const uint8_t* sSA = base + kStageA + kStageB;
         const uint8_t* sSB = sSA + kStageSA;
         const int blk = 2 * s + h;
-        if (g < 4) {
-            f.sa[g] = sSA[(a_frag_row + 32 * g) * 4 + blk];
-            f.sb[g] = sSB[(wave_b_row0<MODE>(wn, g) + l32) * 4 + blk];
-            const uint8_t* rowp = sB + (wave_b_row0<MODE>(wn, g) + l32) * (kBK / 2);
-            const uint4 v = *reinterpret_cast<const uint4*>(rowp + 16 * ((2 * s + h) ^ b_sw));
-            f.b[g] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-        } else if (g < 12) {
-            const int i = (g - 4) >> 1, part = (g - 4) & 1;
+        auto read_a = [&](int i, int part) __attribute__((always_inline)) {
             const uint8_t* rowp = sA + (a_frag_row + 32 * i) * kBK;
             const uint4 v = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * s + 2 * part + h) ^ a_sw));
             if (part == 0) {
@@ -234,15 +239,30 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
             } else {
                 f.a[i][4] = (int)v.x; f.a[i][5] = (int)v.y; f.a[i][6] = (int)v.z; f.a[i][7] = (int)v.w;
             }
+        };
+        if (g == 0) {
+            f.sa[0] = sSA[a_frag_row * 4 + blk];
+            f.sa[1] = sSA[(a_frag_row + 32) * 4 + blk];
+            read_a(0, 0);
+        } else if (g == 1) {
+            read_a(0, 1);
+        } else if (g < 10) {
+            const int j = g - 2;
+            f.sb[j] = sSB[(32 * j + l32) * 4 + blk];
+            const uint8_t* rowp = sB + (32 * j + l32) * (kBK / 2);
+            const uint4 v = *reinterpret_cast<const uint4*>(rowp + 16 * ((2 * s + h) ^ b_sw));
+            f.b[j] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+        } else if (g < 12) {
+            read_a(1, g - 10);
         }
     };
     auto read_all = [&](SubFrags& f, const uint8_t* base, int s) __attribute__((always_inline)) {
 #pragma unroll
         for (int g = 0; g < 12; ++g) read_piece(f, base, s, g);
     };
-    // MFMA number g (0..15) of a sub-step: row tile g/4, column tile g%4.
+    // MFMA number g (0..15) of a sub-step: row tile g/8, column tile g%8.
     auto mfma_one = [&](const SubFrags& f, int g) __attribute__((always_inline)) {
-        const int i = g >> 2, j = g & 3;
+        const int i = g >> 3, j = g & 7;
         const v8i b = v8i{f.b[j][0], f.b[j][1], f.b[j][2], f.b[j][3], 0, 0, 0, 0};
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], b, acc[i][j], 0, 4, 0,
                                                                      f.sa[i], 0, f.sb[j]);
@@ -318,71 +338,73 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
         third = t;
     }
     // ---- epilogue ------------------------------------------------------------
-    // Each lane holds column l32 of 16 rows per MFMA tile.  A 4x4 transpose
-    // inside every quad of lanes (two DPP exchanges and byte permutes) turns
-    // that into 4 consecutive columns of one row, stored straight to global
-    // memory: no LDS, 4-byte (codes) or 8-byte (bf16) stores.
-    const int q4 = lane & 3;   // position inside the quad
-    const int m4 = l32 >> 2;   // quad number: columns 4*m4 .. 4*m4+3 of a 32-column tile
+    // Register r of tile (i, j) is row 64*wm + 32*i + 8*(r/4) + 4*h + r%4;
+    // thanks to the column order of the B rows each lane holds adjacent output
+    // columns of that row, so rows go straight to global memory: 32 lanes
+    // store one contiguous run of the row (no LDS, no lane exchanges).
     if (MODE == kL2) {
         const int N = g.N;
+        uint16_t* out_base = g.out + (int64_t)row0 * N + nt * kBN;  // wave-uniform
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int grp = 0; grp < 4; ++grp) {
-                    // rows 8*grp + 4*h + 0..3 of row tile i, column 32*j + l32
-                    uint32_t x0 = pack_bf16x2(acc[i][j][4 * grp + 0], acc[i][j][4 * grp + 1]);
-                    uint32_t x1 = pack_bf16x2(acc[i][j][4 * grp + 2], acc[i][j][4 * grp + 3]);
-                    quad_transpose_b16(x0, x1, q4);
-                    const int lrow = 128 * wm + 32 * i + 8 * grp + 4 * h + q4;
-                    if (lrow < nrows)
-                        *reinterpret_cast<uint2*>(g.out + (int64_t)(row0 + lrow) * N + nt * kBN +
-                                                  128 * wn + 32 * j + 4 * m4) = make_uint2(x0, x1);
-                }
+            for (int r = 0; r < 16; ++r) {
+                // columns 8*l32 + j, j = 0..7: 16 bytes
+                uint4 v;
+                v.x = pack_bf16x2(acc[i][0][r], acc[i][1][r]);
+                v.y = pack_bf16x2(acc[i][2][r], acc[i][3][r]);
+                v.z = pack_bf16x2(acc[i][4][r], acc[i][5][r]);
+                v.w = pack_bf16x2(acc[i][6][r], acc[i][7][r]);
+                const int lrow = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (lrow < nrows)
+                    *reinterpret_cast<uint4*>(out_base + (uint32_t)(lrow * N + 8 * l32)) = v;
+            }
     } else {
+        // Activation columns 4*l32 + jj (jj = 0..3) of the tile's 128: gate in
+        // tile jj, up in tile jj + 4.  Quantisation group G = l32/8 spans the
+        // 8 lanes l32 = 8G..8G+7, so the group amax is a max over 4 registers
+        // and then over 8 lanes (three DPP steps inside the lane's row).
         const int I = g.I;
+        uint8_t* q_base = g.act_q + (int64_t)row0 * I + nt * 128;          // wave-uniform
+        uint8_t* s_base = g.act_s + (int64_t)row0 * (I / 32) + nt * 4;     // wave-uniform
+        const bool scale_lane = (l32 & 7) == 0;
+        auto rows = [&](auto fast) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                uint32_t codes[16];
-                uint32_t my_scale = 0;
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int rr = 8 * (r >> 2) + 4 * h + (r & 3);
-                    const float gt = round_bf16(acc[i][jj][r]);
-                    const float up = round_bf16(acc[i][jj + 2][r]);
-                    float sl;
-                    if (g.fast_math) {
-                        const float ex = __builtin_amdgcn_exp2f(-gt * 1.4426950408889634f);
-                        sl = gt * __builtin_amdgcn_rcpf(1.0f + ex);
-                    } else {
-                        sl = gt / (1.0f + expf(-gt));
-                    }
-                    const float a = (sl * up) * s_w[128 * wm + 32 * i + rr];
-                    const float amax = half_wave_max(fabsf(a));
-                    const uint32_t b = ue8m0_e4m3(amax);
-                    codes[r] = pack_fp8x2(unscale(a, b), 0.f) & 0xFFu;
-                    if (l32 == r) my_scale = b;  // lane r (< 16) stores the scale of row r
-                }
+                    const int lrow = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const float w = s_w[lrow];
+                    float a[4];
 #pragma unroll
-                for (int grp = 0; grp < 4; ++grp) {
-                    uint32_t x = codes[4 * grp] | (codes[4 * grp + 1] << 8) |
-                                 (codes[4 * grp + 2] << 16) | (codes[4 * grp + 3] << 24);
-                    x = quad_transpose_b8(x, q4);
-                    const int lrow = 128 * wm + 32 * i + 8 * grp + 4 * h + q4;
-                    if (lrow < nrows)
-                        *reinterpret_cast<uint32_t*>(g.act_q + (int64_t)(row0 + lrow) * I + nt * 128 +
-                                                     64 * wn + 32 * jj + 4 * m4) = x;
+                    for (int jj = 0; jj < 4; ++jj) {
+                        // gate and up rounded to bf16 by one conversion
+                        const uint32_t gu = pack_bf16x2(acc[i][jj][r], acc[i][jj + 4][r]);
+                        const float gt = bf16_lo(gu), up = bf16_hi(gu);
+                        float sl;
+                        if (decltype(fast)::value) {
+                            const float ex = __builtin_amdgcn_exp2f(-gt * 1.4426950408889634f);
+                            sl = gt * __builtin_amdgcn_rcpf(1.0f + ex);
+                        } else {
+                            sl = gt / (1.0f + expf(-gt));
+                        }
+                        a[jj] = (sl * up) * w;
+                    }
+                    const float amax = group8_max(fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])),
+                                                        fmaxf(fabsf(a[2]), fabsf(a[3]))));
+                    const uint32_t b = ue8m0_e4m3(amax);
+                    const uint32_t codes = pack_fp8x4(unscale(a[0], b), unscale(a[1], b),
+                                                      unscale(a[2], b), unscale(a[3], b));
+                    if (lrow < nrows) {
+                        *reinterpret_cast<uint32_t*>(q_base + (uint32_t)(lrow * I + 4 * l32)) = codes;
+                        if (scale_lane) s_base[(uint32_t)(lrow * (I / 32) + (l32 >> 3))] = (uint8_t)b;
+                    }
                 }
-                const int srow = 128 * wm + 32 * i + 8 * (l32 >> 2) + 4 * h + (l32 & 3);
-                if (l32 < 16 && srow < nrows)
-                    g.act_s[(int64_t)(row0 + srow) * (I / 32) + (nt * 128 + 64 * wn) / 32 + jj] =
-                        (uint8_t)my_scale;
-            }
-        }
+        };
+        if (g.fast_math)
+            rows(std::true_type{});
+        else
+            rows(std::false_type{});
     }
 }
 

@@ -65,7 +65,6 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]: lane ^ 1
 constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]: lane ^ 2
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7-i inside each 8 lanes
-constexpr int kDppRowMirror = 0x140;      // lane i <-> 15-i inside each 16 lanes
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -79,42 +78,13 @@ __device__ __forceinline__ float quad_max(float v) {
     return v;
 }
 
-// Max over each aligned group of 32 lanes (all lanes get it): four DPP steps
-// reduce each row of 16 lanes, one ds_swizzle (lane ^ 16 inside 32) joins the
-// two rows.
-__device__ __forceinline__ float half_wave_max(float v) {
+// Max over each aligned group of 8 lanes (all lanes get it): mirror inside
+// the 8, then the two quad swaps.
+__device__ __forceinline__ float group8_max(float v) {
+    v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
     v = fmaxf(v, dpp<kDppQuadSwap1>(v));
     v = fmaxf(v, dpp<kDppQuadSwap2>(v));
-    v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
-    v = fmaxf(v, dpp<kDppRowMirror>(v));
-    // swizzle bitmask mode: and 0x1F, or 0, xor 0x10
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
     return v;
-}
-
-// 4x4 transposes inside each quad of lanes.  Lane t of a quad holds element
-// (t, q) of a 4x4 block in part q of its register(s); afterwards it holds
-// element (q, t) in part q.  Two DPP exchanges (lane ^ 1, lane ^ 2) and
-// v_perm_b32 byte selects; t is the lane's position in its quad.
-__device__ __forceinline__ uint32_t quad_transpose_b8(uint32_t x, int t) {
-    const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kDppQuadSwap1, 0xF, 0xF, false);
-    const uint32_t r = __builtin_amdgcn_perm(y, x, (t & 1) ? 0x03070105u : 0x06020400u);
-    const uint32_t z = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)r, kDppQuadSwap2, 0xF, 0xF, false);
-    return __builtin_amdgcn_perm(z, r, (t & 2) ? 0x03020706u : 0x05040100u);
-}
-
-// Same for 16-bit elements: x0 = parts (0, 1), x1 = parts (2, 3).
-__device__ __forceinline__ void quad_transpose_b16(uint32_t& x0, uint32_t& x1, int t) {
-    // exchange 1: even lanes send their high halves, odd lanes their low halves
-    const uint32_t send = __builtin_amdgcn_perm(x1, x0, (t & 1) ? 0x05040100u : 0x07060302u);
-    const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, kDppQuadSwap1, 0xF, 0xF, false);
-    const uint32_t n0 = __builtin_amdgcn_perm(recv, x0, (t & 1) ? 0x03020504u : 0x05040100u);
-    const uint32_t n1 = __builtin_amdgcn_perm(recv, x1, (t & 1) ? 0x03020706u : 0x07060100u);
-    // exchange 2: lanes 0,1 send n1, lanes 2,3 send n0
-    const uint32_t send2 = (t & 2) ? n0 : n1;
-    const uint32_t recv2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send2, kDppQuadSwap2, 0xF, 0xF, false);
-    x0 = (t & 2) ? recv2 : n0;
-    x1 = (t & 2) ? n1 : recv2;
 }
 
 }  // namespace moe
