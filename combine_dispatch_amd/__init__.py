@@ -31,7 +31,7 @@ EXPORTED = ("moe_default_options", "moe_workspace_bytes", "moe_dispatch_workspac
             "moe_fused_forward", "moe_dispatch", "moe_combine", "moe_workspace_views",
             "moe_status_string", "moe_profile_start", "moe_profile_stop",
             "moe_profile_stage_name")
-PROFILE_STAGES = 7
+PROFILE_STAGES = 8
 
 
 class MoeShape(ctypes.Structure):

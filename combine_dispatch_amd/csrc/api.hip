@@ -20,7 +20,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
     size_t seg_hist, seg_base, seg_err, counts, offsets, mtiles, num_mtiles, err_flag;
-    size_t pool_src, slot_to_pool, pool_w, pool_q, pool_s, act_q, act_s, l2_out;
+    size_t pool_src, slot_to_pool, pool_w, pool_q, pool_s, act_q, act_s, l2_out, s1t, s2t, tok_s;
     size_t routing_end;  // bytes moe_dispatch needs
     size_t total;
     int64_t cap;         // pool rows incl. tile padding
@@ -65,6 +65,9 @@ Layout make_layout(const moe_shape_t* s) {
     L.act_q = take((size_t)L.cap * s->I);
     L.act_s = take((size_t)L.cap * (s->I / 32));
     L.l2_out = take((size_t)L.cap * s->H * 2);
+    L.s1t = take((size_t)E * 2 * s->I * (s->H / 32));
+    L.s2t = take((size_t)E * s->H * (s->I / 32));
+    L.tok_s = take((size_t)s->T * (s->H / 32));
     L.total = o;
     return L;
 }
@@ -215,6 +218,8 @@ int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void
     if (s->H % kBN || s->I % 128) return MOE_ERR_UNSUPPORTED;
     if (s->T == 0) return MOE_OK;
     if (!x || !topk_idx || !topk_w || !W1q || !S1 || !W2q || !S2 || !y) return MOE_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(S1) | reinterpret_cast<uintptr_t>(S2)) % 4)
+        return MOE_ERR_INVALID_ARG;  // scale rows are read as 4-byte words
     const Layout L = make_layout(s);
     if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
         return MOE_ERR_WORKSPACE;
@@ -232,15 +237,30 @@ int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void
     uint8_t* act_q = ws + L.act_q;
     uint8_t* act_s = ws + L.act_s;
     uint16_t* l2_out = reinterpret_cast<uint16_t*>(ws + L.l2_out);
+    uint8_t* s1t = ws + L.s1t;
+    uint8_t* s2t = ws + L.s2t;
 
     const int pc = prof_begin(stream);
+    // weight scales into the packed k-major words the GEMMs load per K step
+    hipLaunchKernelGGL(k_scales_kmajor, dim3(2 * I / 64, s->E, (H / 128 + 63) / 64), dim3(256), 0,
+                       stream, reinterpret_cast<const uint32_t*>(S1), reinterpret_cast<uint32_t*>(s1t),
+                       2 * I, H / 128);
+    hipLaunchKernelGGL(k_scales_kmajor, dim3(H / 64, s->E, (I / 128 + 63) / 64), dim3(256), 0,
+                       stream, reinterpret_cast<const uint32_t*>(S2), reinterpret_cast<uint32_t*>(s2t),
+                       H, I / 128);
+    prof_mark(pc, MOE_STAGE_WEIGHT_SCALES, stream);
     int rc = run_routing(s, L, topk_idx, topk_w, ws, counts, offsets, pool_src, slot_to_pool,
                          pool_w, stream, pc);
     if (rc) return rc;
     if (o.debug_validate && (rc = check_routing_flag(ws, L, stream))) return rc;
 
+    uint8_t* tok_s = ws + L.tok_s;
     hipLaunchKernelGGL(k_dispatch_fp8, dim3(T), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(x), H, K, slot_to_pool, pool_q, pool_s);
+                       static_cast<const uint16_t*>(x), H, K, slot_to_pool, pool_q,
+                       static_cast<uint8_t*>(nullptr), tok_s);
+    hipLaunchKernelGGL(k_pool_scales, dim3((unsigned)((L.cap + 255) / 256), H / 128), dim3(256), 0,
+                       stream, reinterpret_cast<const uint32_t*>(tok_s), H / 128, pool_src, offsets,
+                       s->E, K, (int64_t)L.cap, reinterpret_cast<uint32_t*>(pool_s));
     prof_mark(pc, MOE_STAGE_DISPATCH, stream);
 
     GemmArgs g1;
@@ -248,7 +268,8 @@ int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void
     g1.A = pool_q;
     g1.SA = pool_s;
     g1.B = W1q;
-    g1.SB = S1;
+    g1.SB = s1t;
+    g1.sa_step = 4 * L.cap;
     g1.mtiles = reinterpret_cast<const MTile*>(ws + L.mtiles);
     g1.num_mtiles = reinterpret_cast<const int32_t*>(ws + L.num_mtiles);
     g1.Kdim = H;
@@ -267,7 +288,7 @@ int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void
     g2.A = act_q;
     g2.SA = act_s;
     g2.B = W2q;
-    g2.SB = S2;
+    g2.SB = s2t;
     g2.Kdim = I;
     g2.N = H;
     g2.ntiles = H / kBN;
@@ -323,7 +344,7 @@ int moe_dispatch(const moe_shape_t* s, const void* x, const int64_t* topk_idx, c
     if (payload == MOE_PAYLOAD_FP8_E4M3)
         hipLaunchKernelGGL(k_dispatch_fp8, dim3(s->T), dim3(256), 0, stream,
                            static_cast<const uint16_t*>(x), s->H, s->K, slot_to_pool,
-                           static_cast<uint8_t*>(pool), pool_scales);
+                           static_cast<uint8_t*>(pool), pool_scales, static_cast<uint8_t*>(nullptr));
     else
         hipLaunchKernelGGL(k_dispatch_bf16, dim3(s->T), dim3(256), 0, stream,
                            static_cast<const uint16_t*>(x), s->H, s->K, slot_to_pool,
@@ -383,7 +404,7 @@ int moe_profile_stop(double* stage_ms, int* ncalls) {
 }
 
 const char* moe_profile_stage_name(int stage) {
-    static const char* names[MOE_PROFILE_STAGES] = {"route_count", "route_scan", "route_scatter",
+    static const char* names[MOE_PROFILE_STAGES] = {"weight_scales", "route_count", "route_scan", "route_scatter",
                                                     "dispatch", "gemm_l1", "gemm_l2", "combine"};
     return stage >= 0 && stage < MOE_PROFILE_STAGES ? names[stage] : "?";
 }

@@ -112,13 +112,13 @@ __device__ __forceinline__ void dma_x1(uint32_t lds, const void* sbase, uint32_t
                  :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(sbase))
                  : "memory");
 }
-// Wait for this wave's direct loads except the newest 14 (or all), then a
+// Wait for this wave's direct loads except the newest 14 or 21 (or all), then a
 // workgroup barrier.  No memory fence: the data already sits in LDS.
 __device__ __forceinline__ void barrier_after_vmcnt14() {
     asm volatile("s_waitcnt vmcnt(14) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-__device__ __forceinline__ void barrier_after_vmcnt28() {
-    asm volatile("s_waitcnt vmcnt(28) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+__device__ __forceinline__ void barrier_after_vmcnt21() {
+    asm volatile("s_waitcnt vmcnt(21) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 __device__ __forceinline__ void barrier_after_vmcnt0() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -175,33 +175,42 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     const uint32_t b_off1 = (uint32_t)((b_row<MODE>(nt, (tid >> 2) + 64, g.I) - b_r0) * b_ld + 16 * b_chunk);
     const uint32_t b_off2 = (uint32_t)((b_row<MODE>(nt, (tid >> 2) + 128, g.I) - b_r0) * b_ld + 16 * b_chunk);
     const uint32_t b_off3 = (uint32_t)((b_row<MODE>(nt, (tid >> 2) + 192, g.I) - b_r0) * b_ld + 16 * b_chunk);
-    // scales: one dword (4 k-blocks) per row per step; lane l of wave w is row 64 w + l
-    const int s_ld = Kdim / 32;
-    const uint8_t* sa_base = g.SA + (int64_t)row0 * s_ld;
-    const uint32_t sa_off = (uint32_t)(tid * s_ld);
-    const uint8_t* sb_base = g.SB + ((int64_t)e * g.N + b_r0) * s_ld;
-    const uint32_t sb_off = (uint32_t)((b_row<MODE>(nt, tid, g.I) - b_r0) * s_ld);
+    // scales: packed k-major words, one 4-byte word (4 k-blocks) per row per
+    // step, the words of a step contiguous over rows; lane l of wave w loads
+    // tile row 64 w + l (A) and LDS B row 64 w + l (B).
+    const uint8_t* sa_base = g.SA + (int64_t)row0 * 4;
+    const int64_t sa_step = g.sa_step;
+    const uint32_t sa_off = (uint32_t)(tid * 4);
+    const int64_t sb_step = (int64_t)g.N * 4;
+    const uint8_t* sb_base = g.SB + (int64_t)e * (Kdim / 128) * sb_step + (int64_t)b_r0 * 4;
+    const uint32_t sb_off = (uint32_t)((b_row<MODE>(nt, tid, g.I) - b_r0) * 4);
     const uint32_t lds_st0 = lds_addr(st0), lds_st1 = lds_addr(st1), lds_st2 = lds_addr(st2);
     const uint32_t w_dst16 = (uint32_t)(64 * wid * 16);
     const uint32_t w_dst4 = (uint32_t)(64 * wid * 4);
 
-    // 14 loads per wave per step (8 A, 4 B, 2 scale dwords); piece g (0..15)
-    // issues load g, pieces 14 and 15 issue nothing.
-    auto issue_piece = [&](uint32_t st, int k0, int g) __attribute__((always_inline)) {
+    // 14 loads per wave per step (8 A, 4 B, 2 scale dwords), load number
+    // 0..13.  A step's loads go out in two halves of 7, spread one per two
+    // MFMAs: first half-loads h = 0, second h = 1.
+    auto issue_piece = [&](uint32_t st, int kk, int g) __attribute__((always_inline)) {
+        const int k0 = kk * kBK;
         if (g < 8) {
             dma_x4(st + w_dst16 + 4096 * g, a_base + k0, a_off + g * a_step32);
         } else if (g < 12) {
             const uint32_t off = g == 8 ? b_off0 : g == 9 ? b_off1 : g == 10 ? b_off2 : b_off3;
             dma_x4(st + kStageA + w_dst16 + 4096 * (g - 8), b_base + k0 / 2, off);
         } else if (g == 12) {
-            dma_x1(st + kStageA + kStageB + w_dst4, sa_base + k0 / 32, sa_off);
+            dma_x1(st + kStageA + kStageB + w_dst4, sa_base + kk * sa_step, sa_off);
         } else if (g == 13) {
-            dma_x1(st + kStageA + kStageB + kStageSA + w_dst4, sb_base + k0 / 32, sb_off);
+            dma_x1(st + kStageA + kStageB + kStageSA + w_dst4, sb_base + kk * sb_step, sb_off);
         }
     };
-    auto issue = [&](uint32_t st, int kk) __attribute__((always_inline)) {
+    // Load of half `hf` that goes beside MFMA number g (0..15) of a sub-step.
+    auto issue_spread = [&](uint32_t st, int kk, int hf, int g) __attribute__((always_inline)) {
+        if ((g & 1) == 0 && g < 14) issue_piece(st, kk, 7 * hf + (g >> 1));
+    };
+    auto issue_half = [&](uint32_t st, int kk, int hf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int g = 0; g < 14; ++g) issue_piece(st, kk * kBK, g);
+        for (int g = 0; g < 7; ++g) issue_piece(st, kk, 7 * hf + g);
     };
 
     v16f acc[2][8];
@@ -270,20 +279,25 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
 
     // ---- main loop: three LDS stages, sub-step pipelined operands ---------
     // X holds sub-step 0 and Y sub-step 1 of the current step k.  While the 16
-    // MFMAs of X run, Y is read from step k's stage.  Then each wave waits
-    // for its own loads of step k+1 (all LDS reads of step k are done) and
-    // meets the others at a barrier: step k+1's stage is complete and step
-    // k's stage is free, so it is refilled with step k+3 -- those 14 loads
-    // are spread over the MFMAs of Y, while X is read from step k+1's stage.
+    // MFMAs of X run, Y is read from step k's stage and the second half of
+    // step k+2's loads goes out.  Then each wave waits for its own loads of
+    // step k+1 (the newest 14 loads may still fly) and meets the others at a
+    // barrier: step k+1's stage is complete and step k's stage is free (all
+    // its reads are done), so the first half of step k+3's loads goes into it
+    // beside the MFMAs of Y, while X is read from step k+1's stage.  Loads go
+    // out one per two MFMAs, so the load path never backs up the MFMA issue.
     // Every MFMA is fenced together with the reads/loads issued beside it, so
-    // the compiler keeps this order; the loop bodies are branch-free, and the
-    // last three steps run in a second loop that issues no loads and waits
-    // for all of them.
-    issue(lds_st0, 0);
-    if (nk > 1) issue(lds_st1, 1);
-    if (nk > 2) issue(lds_st2, 2);
+    // the compiler keeps this order; the loop body is branch-free, and the
+    // last three steps run in a second loop that issues no new steps.
+    issue_half(lds_st0, 0, 0);
+    issue_half(lds_st0, 0, 1);
+    if (nk > 1) {
+        issue_half(lds_st1, 1, 0);
+        issue_half(lds_st1, 1, 1);
+    }
+    if (nk > 2) issue_half(lds_st2, 2, 0);
     if (nk > 2)
-        barrier_after_vmcnt28();
+        barrier_after_vmcnt21();
     else if (nk > 1)
         barrier_after_vmcnt14();
     else
@@ -295,21 +309,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     const uint8_t* third = st2;
     int k = 0;
     for (; k + 3 < nk; ++k) {
+        const uint32_t dst2 = lds_addr(third);
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
             mfma_one(X, g);
             read_piece(Y, cur, 1, g);
+            issue_spread(dst2, k + 2, 1, g);
             __builtin_amdgcn_sched_barrier(0);
         }
         barrier_after_vmcnt14();
         __builtin_amdgcn_sched_barrier(0);
-        const uint32_t dst = lds_addr(cur);
-        const int k0 = (k + 3) * kBK;
+        const uint32_t dst3 = lds_addr(cur);
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
             mfma_one(Y, g);
             read_piece(X, next, 0, g);
-            issue_piece(dst, k0, g);
+            issue_spread(dst3, k + 3, 0, g);
             __builtin_amdgcn_sched_barrier(0);
         }
         const uint8_t* t = cur;
@@ -318,6 +333,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
         third = t;
     }
     for (; k < nk; ++k) {
+        if (k + 2 < nk) issue_half(lds_addr(third), k + 2, 1);  // the last step's second half
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
             mfma_one(X, g);
@@ -366,7 +383,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
         // and then over 8 lanes (three DPP steps inside the lane's row).
         const int I = g.I;
         uint8_t* q_base = g.act_q + (int64_t)row0 * I + nt * 128;          // wave-uniform
-        uint8_t* s_base = g.act_s + (int64_t)row0 * (I / 32) + nt * 4;     // wave-uniform
+        // scale word of (row, K step nt of the next GEMM), byte G
+        uint8_t* s_base = g.act_s + (int64_t)nt * g.sa_step + (int64_t)row0 * 4;  // wave-uniform
         const bool scale_lane = (l32 & 7) == 0;
         auto rows = [&](auto fast) __attribute__((always_inline)) {
 #pragma unroll
@@ -397,7 +415,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
                                                       unscale(a[2], b), unscale(a[3], b));
                     if (lrow < nrows) {
                         *reinterpret_cast<uint32_t*>(q_base + (uint32_t)(lrow * I + 4 * l32)) = codes;
-                        if (scale_lane) s_base[(uint32_t)(lrow * (I / 32) + (l32 >> 3))] = (uint8_t)b;
+                        if (scale_lane) s_base[(uint32_t)(lrow * 4 + (l32 >> 3))] = (uint8_t)b;
                     }
                 }
         };

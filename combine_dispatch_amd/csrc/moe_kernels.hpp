@@ -30,11 +30,16 @@ struct MTile {
     int32_t expert, row0, nrows, pad;
 };
 
+// Block scales in "packed k-major" layout: one 4-byte word holds the UE8M0
+// bytes of 4 consecutive 32-wide k-blocks (one 128-wide K step), byte b =
+// k-block 4*w + b, and the words of one K step are stored contiguously over
+// rows: word (w, row) at byte 4 * (w * rows_total + row).
 struct GemmArgs {
     const uint8_t* A;    // e4m3 [rows][Kdim]
-    const uint8_t* SA;   // ue8m0 [rows][Kdim/32]
+    const uint8_t* SA;   // packed k-major words [Kdim/128][cap rows]
     const uint8_t* B;    // e2m1x2 [E][N][Kdim/2]
-    const uint8_t* SB;   // ue8m0 [E][N][Kdim/32]
+    const uint8_t* SB;   // packed k-major words per expert [E][Kdim/128][N]
+    int64_t sa_step;     // bytes between K steps of SA (4 * cap)
     const MTile* mtiles;
     const int32_t* num_mtiles;
     int32_t Kdim;        // reduction size
@@ -43,7 +48,7 @@ struct GemmArgs {
     // L1 epilogue
     const float* pool_w; // [rows]
     uint8_t* act_q;      // e4m3 [rows][I]
-    uint8_t* act_s;      // ue8m0 [rows][I/32]
+    uint8_t* act_s;      // packed k-major words [I/128][cap], step sa_step
     int32_t I;
     int32_t fast_math;
     // L2 epilogue
@@ -64,7 +69,14 @@ __global__ void k_route_scatter(const int64_t* __restrict__ topk_idx,
                                 int32_t* __restrict__ slot_to_pool, float* __restrict__ pool_w);
 __global__ void k_dispatch_fp8(const uint16_t* __restrict__ x, int H, int K,
                                const int32_t* __restrict__ slot_to_pool,
-                               uint8_t* __restrict__ pool, uint8_t* __restrict__ pool_s);
+                               uint8_t* __restrict__ pool, uint8_t* __restrict__ pool_s,
+                               uint8_t* __restrict__ tok_s);
+__global__ void k_pool_scales(const uint32_t* __restrict__ tok_s, int W,
+                              const int32_t* __restrict__ pool_src,
+                              const int32_t* __restrict__ offsets, int E, int K, int64_t cap,
+                              uint32_t* __restrict__ pool_s);
+__global__ void k_scales_kmajor(const uint32_t* __restrict__ S, uint32_t* __restrict__ St, int N,
+                                int W);
 __global__ void k_dispatch_bf16(const uint16_t* __restrict__ x, int H, int K,
                                 const int32_t* __restrict__ slot_to_pool,
                                 uint16_t* __restrict__ pool);

@@ -173,11 +173,14 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(
 // a4: gather + quantise.  One block per token row.  Each lane owns 8
 // consecutive columns (one 16-byte load), a quad of lanes owns one 32-column
 // scale group: amax over the quad, UE8M0 scale, e4m3 codes, then the 8 code
-// bytes go to every valid pool row of the token.
+// bytes go to every valid pool row of the token.  The scale bytes go either
+// to every pool row of the token (pool_s, [rows][H/32]) or once to the token
+// (tok_s, [T][H/32]); a null pointer skips that form.
 __global__ __launch_bounds__(256) void k_dispatch_fp8(const uint16_t* __restrict__ x, int H,
                                                      int K, const int32_t* __restrict__ slot_to_pool,
                                                      uint8_t* __restrict__ pool,
-                                                     uint8_t* __restrict__ pool_s) {
+                                                     uint8_t* __restrict__ pool_s,
+                                                     uint8_t* __restrict__ tok_s) {
     __shared__ int32_t rows[64];
     const int64_t t = blockIdx.x;
     if (threadIdx.x < K) rows[threadIdx.x] = slot_to_pool[t * K + threadIdx.x];
@@ -195,12 +198,51 @@ __global__ __launch_bounds__(256) void k_dispatch_fp8(const uint16_t* __restrict
         uint2 q;
         q.x = pack_fp8x4(unscale(f[0], b), unscale(f[1], b), unscale(f[2], b), unscale(f[3], b));
         q.y = pack_fp8x4(unscale(f[4], b), unscale(f[5], b), unscale(f[6], b), unscale(f[7], b));
+        if (tok_s && (threadIdx.x & 3) == 0) tok_s[t * (H / 32) + c0 / 32] = (uint8_t)b;
         for (int k = 0; k < K; ++k) {
             const int32_t r = rows[k];
             if (r < 0) continue;
             *reinterpret_cast<uint2*>(pool + (int64_t)r * H + c0) = q;
-            if ((threadIdx.x & 3) == 0) pool_s[(int64_t)r * (H / 32) + c0 / 32] = (uint8_t)b;
+            if (pool_s && (threadIdx.x & 3) == 0) pool_s[(int64_t)r * (H / 32) + c0 / 32] = (uint8_t)b;
         }
+    }
+}
+
+// Pool scales in packed k-major words (the layout the GEMM loads per K step):
+// word (w, r) = word w of token pool_src[r] / K's scale row.  Thread per
+// (pool row, word); consecutive threads write consecutive rows.  Rows from R
+// on are left as they are.
+__global__ __launch_bounds__(256) void k_pool_scales(const uint32_t* __restrict__ tok_s, int W,
+                                                    const int32_t* __restrict__ pool_src,
+                                                    const int32_t* __restrict__ offsets, int E,
+                                                    int K, int64_t cap,
+                                                    uint32_t* __restrict__ pool_s) {
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int w = blockIdx.y;
+    if (r >= offsets[E]) return;
+    const int64_t t = pool_src[r] / K;
+    pool_s[(int64_t)w * cap + r] = tok_s[t * W + w];
+}
+
+// Weight scales [E][N][W words] (row-major, W = Kdim/128 words of 4 UE8M0
+// bytes per row) -> packed k-major [E][W][N].  Block (n-tile of 64 rows,
+// expert, word tile of 64): coalesced row reads into an LDS tile, coalesced
+// column writes out of it.
+__global__ __launch_bounds__(256) void k_scales_kmajor(const uint32_t* __restrict__ S,
+                                                      uint32_t* __restrict__ St, int N, int W) {
+    __shared__ uint32_t tile[64][65];
+    const int n0 = blockIdx.x * 64, e = blockIdx.y, w0 = blockIdx.z * 64;
+    const int nw = min(64, W - w0);
+    const uint32_t* src = S + ((int64_t)e * N + n0) * W + w0;
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int r = i >> 6, w = i & 63;
+        if (w < nw) tile[w][r] = src[(int64_t)r * W + w];
+    }
+    __syncthreads();
+    uint32_t* dst = St + ((int64_t)e * W + w0) * N + n0;
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int w = i >> 6, r = i & 63;
+        if (w < nw) dst[(int64_t)w * N + r] = tile[w][r];
     }
 }
 

@@ -94,9 +94,9 @@ size_t moe_dispatch_workspace_bytes(const moe_shape_t* s);
  *   topk_idx  int64 [T][K]   expert per slot; < 0 masked
  *   topk_w    fp32  [T][K]   routing weights (applied to the SwiGLU output)
  *   W1q       e2m1x2 [E][2I][H/2]  rows 0..I-1 gate, I..2I-1 up
- *   S1        ue8m0 [E][2I][H/32]
+ *   S1        ue8m0 [E][2I][H/32]  (4-byte aligned)
  *   W2q       e2m1x2 [E][H][I/2]
- *   S2        ue8m0 [E][H][I/32]
+ *   S2        ue8m0 [E][H][I/32]   (4-byte aligned)
  *   y         bf16  [T][H], fully overwritten (an all-masked token gives +0)
  *   workspace device buffer of at least moe_workspace_bytes(s) bytes, 256-byte
  *             aligned; its contents on entry do not matter.
@@ -154,10 +154,16 @@ int moe_combine(const moe_shape_t* s, const void* pool_out, const int32_t* slot_
 
 /* Byte offsets of intermediates inside a moe_fused_forward workspace, so that
  * tests can read them after a call (all -1 on a bad shape). */
+/* The block scales of the pool and of the activation are stored as packed
+ * k-major words: the word for row r and K step w (128 columns) holds the
+ * UE8M0 bytes of the row's 32-column groups 4w..4w+3 (byte b = group 4w+b)
+ * at byte offset 4 * (w * cap + r), so one K step of a row tile is one
+ * contiguous run (the pages' SF buffers pack 4 UE8M0 per 128 columns, [P3]
+ * appendix A.1). */
 typedef struct {
     int64_t counts, offsets, pool_src, slot_to_pool, pool_w; /* routing arrays */
-    int64_t pool_q, pool_s;   /* e4m3 [cap][H], ue8m0 [cap][H/32] */
-    int64_t act_q, act_s;     /* e4m3 [cap][I], ue8m0 [cap][I/32] */
+    int64_t pool_q, pool_s;   /* e4m3 [cap][H], packed k-major words [H/128][cap] */
+    int64_t act_q, act_s;     /* e4m3 [cap][I], packed k-major words [I/128][cap] */
     int64_t l2_out;           /* bf16 [cap][H] */
     int64_t capacity_rows;    /* cap = T*K + tile padding */
 } moe_workspace_views_t;

@@ -17,7 +17,8 @@ extern "C" {
 
 /* Stages of moe_fused_forward, in launch order. */
 enum {
-    MOE_STAGE_ROUTE_COUNT = 0, /* a1: per-segment expert histogram */
+    MOE_STAGE_WEIGHT_SCALES = 0, /* weight scales -> packed k-major words */
+    MOE_STAGE_ROUTE_COUNT,     /* a1: per-segment expert histogram */
     MOE_STAGE_ROUTE_SCAN,      /* a2: offsets, segment bases, m-tile table */
     MOE_STAGE_ROUTE_SCATTER,   /* a3: stable rank -> pool_src, slot_to_pool, pool_w */
     MOE_STAGE_DISPATCH,        /* a4: gather + e4m3 quantisation into the pool */
@@ -27,7 +28,7 @@ enum {
     MOE_PROFILE_STAGES
 };
 
-/* Start recording (creates 8 events per call slot; host allocation only).
+/* Start recording (creates MOE_PROFILE_STAGES + 1 events per call slot; host allocation only).
  * Returns 0, or MOE_ERR_INVALID_ARG for max_calls outside 1..4096, or
  * MOE_ERR_DEVICE if the events cannot be created. */
 int moe_profile_start(int max_calls);

@@ -52,10 +52,16 @@ def view(workspace: torch.Tensor, inp: dict, name: str, rows: int | None = None)
         "act_s": (np.uint8, (TK, I // 32)), "l2_out": (np.uint16, (TK, H)),
     }
     dt, shape = spec[name]
+    off = v[name]
+    if name in ("pool_s", "act_s"):
+        # packed k-major words: word (w, r) at 4 * (w * cap + r), byte b = group 4w + b
+        cap, groups = v["capacity_rows"], shape[1]
+        raw = workspace[off:off + cap * groups].cpu().numpy()
+        rm = raw.reshape(groups // 4, cap, 4).transpose(1, 0, 2).reshape(cap, groups)
+        return np.ascontiguousarray(rm[:(rows if rows is not None else shape[0])])
     if rows is not None:
         shape = (rows,) + shape[1:]
     nbytes = int(np.prod(shape)) * np.dtype(dt).itemsize
-    off = v[name]
     return workspace[off:off + nbytes].cpu().numpy().view(dt).reshape(shape)
 
 
