@@ -381,42 +381,60 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
         // tile jj, up in tile jj + 4.  Quantisation group G = l32/8 spans the
         // 8 lanes l32 = 8G..8G+7, so the group amax is a max over 4 registers
         // and then over 8 lanes (three DPP steps inside the lane's row).
+        // Rows go in blocks of 4 consecutive rows (registers r = 4*rq + 0..3),
+        // computed without branches so the four rows interleave; then each
+        // row's 4 code bytes are one dword store, and lanes l32 = 8G + rr
+        // (rr < 4) store the scale byte of row rr, group G: one byte store per
+        // block writes the block's 16 contiguous scale bytes.
         const int I = g.I;
-        uint8_t* q_base = g.act_q + (int64_t)row0 * I + nt * 128;          // wave-uniform
-        // scale word of (row, K step nt of the next GEMM), byte G
+        uint8_t* q_base = g.act_q + (int64_t)row0 * I + nt * 128;                 // wave-uniform
         uint8_t* s_base = g.act_s + (int64_t)nt * g.sa_step + (int64_t)row0 * 4;  // wave-uniform
-        const bool scale_lane = (l32 & 7) == 0;
+        const int rsel = l32 & 7;
         auto rows = [&](auto fast) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int lrow = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const float w = s_w[lrow];
-                    float a[4];
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int lrow0 = 64 * wm + 32 * i + 8 * rq + 4 * h;
+                    const float4 w4 = *reinterpret_cast<const float4*>(s_w + lrow0);
+                    const float wr[4] = {w4.x, w4.y, w4.z, w4.w};
+                    float a[4][4];
+                    uint32_t m[4];
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        // gate and up rounded to bf16 by one conversion
-                        const uint32_t gu = pack_bf16x2(acc[i][jj][r], acc[i][jj + 4][r]);
-                        const float gt = bf16_lo(gu), up = bf16_hi(gu);
-                        float sl;
-                        if (decltype(fast)::value) {
-                            const float ex = __builtin_amdgcn_exp2f(-gt * 1.4426950408889634f);
-                            sl = gt * __builtin_amdgcn_rcpf(1.0f + ex);
-                        } else {
-                            sl = gt / (1.0f + expf(-gt));
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int r = 4 * rq + rr;
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            // gate and up rounded to bf16 by one conversion
+                            const uint32_t gu = pack_bf16x2(acc[i][jj][r], acc[i][jj + 4][r]);
+                            const float gt = bf16_lo(gu), up = bf16_hi(gu);
+                            float sl;
+                            if (decltype(fast)::value) {
+                                const float ex = __builtin_amdgcn_exp2f(-gt * 1.4426950408889634f);
+                                sl = gt * __builtin_amdgcn_rcpf(1.0f + ex);
+                            } else {
+                                sl = gt / (1.0f + expf(-gt));
+                            }
+                            a[rr][jj] = (sl * up) * wr[rr];
                         }
-                        a[jj] = (sl * up) * w;
+                        m[rr] = __float_as_uint(fmaxf(fmaxf(fabsf(a[rr][0]), fabsf(a[rr][1])),
+                                                      fmaxf(fabsf(a[rr][2]), fabsf(a[rr][3]))));
                     }
-                    const float amax = group8_max(fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])),
-                                                        fmaxf(fabsf(a[2]), fabsf(a[3]))));
-                    const uint32_t b = ue8m0_e4m3(amax);
-                    const uint32_t codes = pack_fp8x4(unscale(a[0], b), unscale(a[1], b),
-                                                      unscale(a[2], b), unscale(a[3], b));
-                    if (lrow < nrows) {
-                        *reinterpret_cast<uint32_t*>(q_base + (uint32_t)(lrow * I + 4 * l32)) = codes;
-                        if (scale_lane) s_base[(uint32_t)(lrow * 4 + (l32 >> 3))] = (uint8_t)b;
+                    group8_max_u32x4(m);
+                    uint32_t codes[4], b[4];
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        b[rr] = ue8m0_e4m3_bits(m[rr]);
+                        codes[rr] = pack_fp8x4(unscale(a[rr][0], b[rr]), unscale(a[rr][1], b[rr]),
+                                               unscale(a[rr][2], b[rr]), unscale(a[rr][3], b[rr]));
                     }
+                    const uint32_t bsel = rsel == 0 ? b[0] : rsel == 1 ? b[1] : rsel == 2 ? b[2] : b[3];
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+                        if (lrow0 + rr < nrows)
+                            *reinterpret_cast<uint32_t*>(q_base + (uint32_t)((lrow0 + rr) * I + 4 * l32)) = codes[rr];
+                    if (rsel < 4 && lrow0 + rsel < nrows)
+                        s_base[(uint32_t)((lrow0 + rsel) * 4 + (l32 >> 3))] = (uint8_t)bsel;
                 }
         };
         if (g.fast_math)

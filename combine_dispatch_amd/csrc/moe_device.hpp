@@ -54,6 +54,12 @@ __device__ __forceinline__ uint32_t ue8m0_e4m3(float amax) {
     return (uint32_t)b;
 }
 
+// Same from the bits of a non-negative finite amax.
+__device__ __forceinline__ uint32_t ue8m0_e4m3_bits(uint32_t bits) {
+    const int b = (int)(bits >> 23) - 8 + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    return (uint32_t)(b < 0 ? 0 : (b > 254 ? 254 : b));
+}
+
 // v * 2^(127-b): exact (v_ldexp_f32).
 __device__ __forceinline__ float unscale(float v, uint32_t b) {
     return __builtin_amdgcn_ldexpf(v, 127 - (int)b);
@@ -76,6 +82,22 @@ __device__ __forceinline__ float quad_max(float v) {
     v = fmaxf(v, dpp<kDppQuadSwap1>(v));
     v = fmaxf(v, dpp<kDppQuadSwap2>(v));
     return v;
+}
+
+// Max over each aligned group of 8 lanes of four non-negative values held as
+// float bits (unsigned order = float order), all lanes get them: mirror
+// inside the 8, then the two quad swaps; the four chains interleave.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ void group8_max_u32x4(uint32_t (&m)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m[q] = max(m[q], dpp_u32<kDppRowHalfMirror>(m[q]));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m[q] = max(m[q], dpp_u32<kDppQuadSwap1>(m[q]));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m[q] = max(m[q], dpp_u32<kDppQuadSwap2>(m[q]));
 }
 
 // Max over each aligned group of 8 lanes (all lanes get it): mirror inside
