@@ -73,12 +73,19 @@ __device__ __forceinline__ int tile_of_block(int bid, int nblk) {
 }
 
 // MFMA operands of one 64-wide K sub-step for one wave: A fragments of its 2
-// row tiles, B fragments of the 8 column tiles, per-lane scale registers.
+// row tiles, B fragments of the 8 column tiles.
 struct SubFrags {
     v8i a[2];
     v4i b[8];
-    int sa[2];
-    int sb[8];
+};
+
+// Scale words of one K step for one wave: the word of each of its 2 A row
+// tiles and 8 B column tiles (lane row / column l%32).  Words hold the bytes
+// of k-blocks (0, 2, 1, 3) of the step; shifted right by 16 in lanes 32-63
+// they hold k-block 2s + l/32 in byte s, so sub-step s selects byte s.
+struct ScaleWords {
+    int a[2];
+    int b[8];
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -163,27 +170,32 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     // row q/8, physical chunk q%8, holding logical chunk (q%8) ^ ((row/2)%8).
     const int a_chunk = (tid & 7) ^ ((tid >> 4) & 7);
     const uint32_t a_off = (uint32_t)((tid >> 3) * Kdim + 16 * a_chunk);
-    const uint32_t a_step32 = (uint32_t)(32 * Kdim);  // 32 rows = next i
     const uint8_t* a_base = g.A + (int64_t)row0 * Kdim;
     // B: 1024 chunks; chunk q = tid + 256 i is LDS row q/4 (B row b_row(q/4)),
     // physical chunk q%4, logical chunk (q%4) ^ ((row/4)%4).
     const int b_chunk = (tid & 3) ^ ((tid >> 4) & 3);
     const int b_ld = Kdim / 2;
-    const uint8_t* b_base = g.B + ((int64_t)e * g.N + b_row<MODE>(nt, 0, g.I)) * b_ld;
     const int b_r0 = b_row<MODE>(nt, 0, g.I);
-    const uint32_t b_off0 = (uint32_t)((b_row<MODE>(nt, (tid >> 2), g.I) - b_r0) * b_ld + 16 * b_chunk);
-    const uint32_t b_off1 = (uint32_t)((b_row<MODE>(nt, (tid >> 2) + 64, g.I) - b_r0) * b_ld + 16 * b_chunk);
-    const uint32_t b_off2 = (uint32_t)((b_row<MODE>(nt, (tid >> 2) + 128, g.I) - b_r0) * b_ld + 16 * b_chunk);
-    const uint32_t b_off3 = (uint32_t)((b_row<MODE>(nt, (tid >> 2) + 192, g.I) - b_r0) * b_ld + 16 * b_chunk);
+    const uint8_t* b_base = g.B + ((int64_t)e * g.N + b_r0) * b_ld;
+    // Load q (0..3) covers LDS B rows 64q + tid/4; with the column order of
+    // b_row its expert rows differ from those of load 0 by a wave-uniform
+    // number of rows, which goes into the scalar base.
+    const uint32_t b_off = (uint32_t)((b_row<MODE>(nt, (tid >> 2), g.I) - b_r0) * b_ld + 16 * b_chunk);
+    const int b_dq1 = b_row<MODE>(0, 64, g.I) - b_row<MODE>(0, 0, g.I);
+    const int b_dq2 = b_row<MODE>(0, 128, g.I) - b_row<MODE>(0, 0, g.I);
+    const int b_dq3 = b_row<MODE>(0, 192, g.I) - b_row<MODE>(0, 0, g.I);
     // scales: packed k-major words, one 4-byte word (4 k-blocks) per row per
-    // step, the words of a step contiguous over rows; lane l of wave w loads
-    // tile row 64 w + l (A) and LDS B row 64 w + l (B).
+    // step, the words of a step contiguous over rows.  LDS word p of the A
+    // scales is row tile p%2 of wave p/64, lane row (p%64)/2, so a lane's two
+    // words are adjacent; LDS word p of the B scales is column tile p%8,
+    // lane column p/8, so a lane's eight words are adjacent.  Thread tid loads
+    // LDS word tid of each, so it picks its source row accordingly.
     const uint8_t* sa_base = g.SA + (int64_t)row0 * 4;
     const int64_t sa_step = g.sa_step;
-    const uint32_t sa_off = (uint32_t)(tid * 4);
+    const uint32_t sa_off = (uint32_t)(4 * ((tid & ~63) + 32 * (tid & 1) + ((tid & 63) >> 1)));
     const int64_t sb_step = (int64_t)g.N * 4;
     const uint8_t* sb_base = g.SB + (int64_t)e * (Kdim / 128) * sb_step + (int64_t)b_r0 * 4;
-    const uint32_t sb_off = (uint32_t)((b_row<MODE>(nt, tid, g.I) - b_r0) * 4);
+    const uint32_t sb_off = (uint32_t)((b_row<MODE>(nt, 32 * (tid & 7) + (tid >> 3), g.I) - b_r0) * 4);
     const uint32_t lds_st0 = lds_addr(st0), lds_st1 = lds_addr(st1), lds_st2 = lds_addr(st2);
     const uint32_t w_dst16 = (uint32_t)(64 * wid * 16);
     const uint32_t w_dst4 = (uint32_t)(64 * wid * 4);
@@ -194,10 +206,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     auto issue_piece = [&](uint32_t st, int kk, int g) __attribute__((always_inline)) {
         const int k0 = kk * kBK;
         if (g < 8) {
-            dma_x4(st + w_dst16 + 4096 * g, a_base + k0, a_off + g * a_step32);
+            dma_x4(st + w_dst16 + 4096 * g, a_base + k0 + (int64_t)g * 32 * Kdim, a_off);
         } else if (g < 12) {
-            const uint32_t off = g == 8 ? b_off0 : g == 9 ? b_off1 : g == 10 ? b_off2 : b_off3;
-            dma_x4(st + kStageA + w_dst16 + 4096 * (g - 8), b_base + k0 / 2, off);
+            const int dq = g == 8 ? 0 : g == 9 ? b_dq1 : g == 10 ? b_dq2 : b_dq3;
+            dma_x4(st + kStageA + w_dst16 + 4096 * (g - 8), b_base + k0 / 2 + (int64_t)dq * b_ld, b_off);
         } else if (g == 12) {
             dma_x1(st + kStageA + kStageB + w_dst4, sa_base + kk * sa_step, sa_off);
         } else if (g == 13) {
@@ -231,15 +243,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     // Operand reads of sub-step s (0 or 1) of the step held in an LDS stage,
     // split into the pieces read next to each MFMA, in the order the next
     // sub-step's MFMAs (row tile 0 with column tiles 0..7, then row tile 1)
-    // consume them: A scales and row tile 0, then each column tile with its
-    // scale, then row tile 1.  Each lane reads the scale byte of its own
-    // k-block, so no shifts are needed.
+    // consume them: row tile 0, the column tiles, row tile 1.
     auto read_piece = [&](SubFrags& f, const uint8_t* base, int s, int g) __attribute__((always_inline)) {
         const uint8_t* sA = base;
         const uint8_t* sB = base + kStageA;
-        const uint8_t* sSA = base + kStageA + kStageB;
-        const uint8_t* sSB = sSA + kStageSA;
-        const int blk = 2 * s + h;
         auto read_a = [&](int i, int part) __attribute__((always_inline)) {
             const uint8_t* rowp = sA + (a_frag_row + 32 * i) * kBK;
             const uint4 v = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * s + 2 * part + h) ^ a_sw));
@@ -249,15 +256,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
                 f.a[i][4] = (int)v.x; f.a[i][5] = (int)v.y; f.a[i][6] = (int)v.z; f.a[i][7] = (int)v.w;
             }
         };
-        if (g == 0) {
-            f.sa[0] = sSA[a_frag_row * 4 + blk];
-            f.sa[1] = sSA[(a_frag_row + 32) * 4 + blk];
-            read_a(0, 0);
-        } else if (g == 1) {
-            read_a(0, 1);
+        if (g < 2) {
+            read_a(0, g);
         } else if (g < 10) {
             const int j = g - 2;
-            f.sb[j] = sSB[(32 * j + l32) * 4 + blk];
             const uint8_t* rowp = sB + (32 * j + l32) * (kBK / 2);
             const uint4 v = *reinterpret_cast<const uint4*>(rowp + 16 * ((2 * s + h) ^ b_sw));
             f.b[j] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
@@ -265,17 +267,52 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
             read_a(1, g - 10);
         }
     };
-    auto read_all = [&](SubFrags& f, const uint8_t* base, int s) __attribute__((always_inline)) {
+    // Scale words of a step: part 0 the two A words (8 bytes), parts 1 and 2
+    // the B words 0-3 and 4-7 (16 bytes each).
+    auto read_scales = [&](ScaleWords& w, const uint8_t* base, int part) __attribute__((always_inline)) {
+        const uint8_t* sSA = base + kStageA + kStageB;
+        const uint8_t* sSB = sSA + kStageSA;
+        if (part == 0) {
+            const uint2 v = *reinterpret_cast<const uint2*>(sSA + 256 * wm + 8 * l32);
+            w.a[0] = (int)v.x; w.a[1] = (int)v.y;
+        } else {
+            const uint4 v = *reinterpret_cast<const uint4*>(sSB + 32 * l32 + 16 * (part - 1));
+            const int j0 = 4 * (part - 1);
+            w.b[j0] = (int)v.x; w.b[j0 + 1] = (int)v.y; w.b[j0 + 2] = (int)v.z; w.b[j0 + 3] = (int)v.w;
+        }
+    };
+    auto read_all = [&](SubFrags& f, ScaleWords& w, const uint8_t* base, int s) __attribute__((always_inline)) {
 #pragma unroll
         for (int g = 0; g < 12; ++g) read_piece(f, base, s, g);
+#pragma unroll
+        for (int part = 0; part < 3; ++part) read_scales(w, base, part);
     };
-    // MFMA number g (0..15) of a sub-step: row tile g/8, column tile g%8.
-    auto mfma_one = [&](const SubFrags& f, int g) __attribute__((always_inline)) {
+    // Scale words read beside the pieces of the next step's sub-step 0.
+    auto read_piece_and_scales = [&](SubFrags& f, ScaleWords& w, const uint8_t* base, int g) __attribute__((always_inline)) {
+        read_piece(f, base, 0, g);
+        if (g == 0) read_scales(w, base, 0);
+        if (g == 1) read_scales(w, base, 1);
+        if (g == 5) read_scales(w, base, 2);
+    };
+    // Words as read -> words the MFMAs use (see ScaleWords); done beside the
+    // first MFMA that needs each.
+    const int hs = 16 * h;
+    auto shift_for = [&](ScaleWords& c, const ScaleWords& n, int g) __attribute__((always_inline)) {
+        if (g == 0) { c.a[0] = (int)((uint32_t)n.a[0] >> hs); c.b[0] = (int)((uint32_t)n.b[0] >> hs); }
+        if (g > 0 && g < 8) c.b[g] = (int)((uint32_t)n.b[g] >> hs);
+        if (g == 8) c.a[1] = (int)((uint32_t)n.a[1] >> hs);
+    };
+    // MFMA number g (0..15) of sub-step S: row tile g/8, column tile g%8;
+    // scale byte S of the words.
+    auto mfma_one = [&](const SubFrags& f, const ScaleWords& w, auto sub, int g) __attribute__((always_inline)) {
+        constexpr int S = decltype(sub)::value;
         const int i = g >> 3, j = g & 7;
         const v8i b = v8i{f.b[j][0], f.b[j][1], f.b[j][2], f.b[j][3], 0, 0, 0, 0};
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], b, acc[i][j], 0, 4, 0,
-                                                                     f.sa[i], 0, f.sb[j]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], b, acc[i][j], 0, 4, S,
+                                                                     w.a[i], S, w.b[j]);
     };
+    const std::integral_constant<int, 0> sub0;
+    const std::integral_constant<int, 1> sub1;
 
     // ---- main loop: three LDS stages, sub-step pipelined operands ---------
     // X holds sub-step 0 and Y sub-step 1 of the current step k.  While the 16
@@ -303,7 +340,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     else
         barrier_after_vmcnt0();
     SubFrags X, Y;
-    read_all(X, st0, 0);
+    ScaleWords Wc, Wn;  // words in use (shifted), words of the next step as read
+    read_all(X, Wn, st0, 0);
     const uint8_t* cur = st0;
     const uint8_t* next = st1;
     const uint8_t* third = st2;
@@ -312,7 +350,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
         const uint32_t dst2 = lds_addr(third);
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
-            mfma_one(X, g);
+            shift_for(Wc, Wn, g);
+            mfma_one(X, Wc, sub0, g);
             read_piece(Y, cur, 1, g);
             issue_spread(dst2, k + 2, 1, g);
             __builtin_amdgcn_sched_barrier(0);
@@ -322,8 +361,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
         const uint32_t dst3 = lds_addr(cur);
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
-            mfma_one(Y, g);
-            read_piece(X, next, 0, g);
+            mfma_one(Y, Wc, sub1, g);
+            read_piece_and_scales(X, Wn, next, g);
             issue_spread(dst3, k + 3, 0, g);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -332,50 +371,67 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
         next = third;
         third = t;
     }
-    for (; k < nk; ++k) {
-        if (k + 2 < nk) issue_half(lds_addr(third), k + 2, 1);  // the last step's second half
+    // The last min(nk, 3) steps issue no new steps.  Each is straight-line
+    // code (a branch inside would let the compiler sink MFMAs past the
+    // barrier); the first of them (when nk >= 3) sends the second half of the
+    // last step's loads, and its barrier then waits for step k+1 only.
+    auto tail_step = [&](auto issue_tag) __attribute__((always_inline)) {
+        constexpr bool kIssue = decltype(issue_tag)::value;
+        if (kIssue) issue_half(lds_addr(third), k + 2, 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
-            mfma_one(X, g);
+            shift_for(Wc, Wn, g);
+            mfma_one(X, Wc, sub0, g);
             read_piece(Y, cur, 1, g);
             __builtin_amdgcn_sched_barrier(0);
         }
-        barrier_after_vmcnt0();
+        if (kIssue)
+            barrier_after_vmcnt14();
+        else
+            barrier_after_vmcnt0();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
-            mfma_one(Y, g);
-            read_piece(X, next, 0, g);  // on the last step this reads a stale stage, unused
+            mfma_one(Y, Wc, sub1, g);
+            read_piece_and_scales(X, Wn, next, g);  // on the last step: a stale stage, unused
             __builtin_amdgcn_sched_barrier(0);
         }
         const uint8_t* t = cur;
         cur = next;
         next = third;
         third = t;
-    }
+        ++k;
+    };
+    if (nk >= 3) tail_step(std::true_type{});
+    while (k < nk) tail_step(std::false_type{});
     // ---- epilogue ------------------------------------------------------------
     // Register r of tile (i, j) is row 64*wm + 32*i + 8*(r/4) + 4*h + r%4;
     // thanks to the column order of the B rows each lane holds adjacent output
     // columns of that row, so rows go straight to global memory: 32 lanes
     // store one contiguous run of the row (no LDS, no lane exchanges).
+    // Full tiles (the common case) store without row checks, so the
+    // epilogue is straight-line code; partial tiles check each row.
     if (MODE == kL2) {
         const int N = g.N;
-        uint16_t* out_base = g.out + (int64_t)row0 * N + nt * kBN;  // wave-uniform
+        uint8_t* out_base = reinterpret_cast<uint8_t*>(g.out + (int64_t)row0 * N + nt * kBN);  // wave-uniform
+        auto rows = [&](auto partial) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                // columns 8*l32 + j, j = 0..7: 16 bytes
-                uint4 v;
-                v.x = pack_bf16x2(acc[i][0][r], acc[i][1][r]);
-                v.y = pack_bf16x2(acc[i][2][r], acc[i][3][r]);
-                v.z = pack_bf16x2(acc[i][4][r], acc[i][5][r]);
-                v.w = pack_bf16x2(acc[i][6][r], acc[i][7][r]);
-                const int lrow = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (lrow < nrows)
-                    *reinterpret_cast<uint4*>(out_base + (uint32_t)(lrow * N + 8 * l32)) = v;
-            }
+                for (int r = 0; r < 16; ++r) {
+                    // columns 8*l32 + j, j = 0..7: 16 bytes
+                    uint4 v;
+                    v.x = pack_bf16x2(acc[i][0][r], acc[i][1][r]);
+                    v.y = pack_bf16x2(acc[i][2][r], acc[i][3][r]);
+                    v.z = pack_bf16x2(acc[i][4][r], acc[i][5][r]);
+                    v.w = pack_bf16x2(acc[i][6][r], acc[i][7][r]);
+                    const int lrow = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (!decltype(partial)::value || lrow < nrows)
+                        *reinterpret_cast<uint4*>(out_base + (uint32_t)(2 * (lrow * N + 8 * l32))) = v;
+                }
+        };
+        rows(std::true_type{});
     } else {
         // Activation columns 4*l32 + jj (jj = 0..3) of the tile's 128: gate in
         // tile jj, up in tile jj + 4.  Quantisation group G = l32/8 spans the
@@ -390,7 +446,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
         uint8_t* q_base = g.act_q + (int64_t)row0 * I + nt * 128;                 // wave-uniform
         uint8_t* s_base = g.act_s + (int64_t)nt * g.sa_step + (int64_t)row0 * 4;  // wave-uniform
         const int rsel = l32 & 7;
-        auto rows = [&](auto fast) __attribute__((always_inline)) {
+        const int G = l32 >> 3, gbyte = ((G & 1) << 1) | (G >> 1);
+        auto rows = [&](auto fast, auto partial) __attribute__((always_inline)) {
+            constexpr bool kPartial = decltype(partial)::value;
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -431,16 +489,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
                     const uint32_t bsel = rsel == 0 ? b[0] : rsel == 1 ? b[1] : rsel == 2 ? b[2] : b[3];
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
-                        if (lrow0 + rr < nrows)
+                        if (!kPartial || lrow0 + rr < nrows)
                             *reinterpret_cast<uint32_t*>(q_base + (uint32_t)((lrow0 + rr) * I + 4 * l32)) = codes[rr];
-                    if (rsel < 4 && lrow0 + rsel < nrows)
-                        s_base[(uint32_t)((lrow0 + rsel) * 4 + (l32 >> 3))] = (uint8_t)bsel;
+                    // group G is byte (0, 2, 1, 3)[G] of the word
+                    if (rsel < 4 && (!kPartial || lrow0 + rsel < nrows))
+                        s_base[(uint32_t)((lrow0 + rsel) * 4 + gbyte)] = (uint8_t)bsel;
                 }
         };
         if (g.fast_math)
-            rows(std::true_type{});
+            rows(std::true_type{}, std::true_type{});
         else
-            rows(std::false_type{});
+            rows(std::false_type{}, std::true_type{});
     }
 }
 

@@ -60,6 +60,12 @@ __device__ __forceinline__ uint32_t ue8m0_e4m3_bits(uint32_t bits) {
     return (uint32_t)(b < 0 ? 0 : (b > 254 ? 254 : b));
 }
 
+// Bytes (0, 1, 2, 3) -> (0, 2, 1, 3): the order of k-blocks inside a packed
+// scale word.
+__device__ __forceinline__ uint32_t swap_bytes12(uint32_t v) {
+    return (v & 0xFF0000FFu) | ((v >> 8) & 0x0000FF00u) | ((v << 8) & 0x00FF0000u);
+}
+
 // v * 2^(127-b): exact (v_ldexp_f32).
 __device__ __forceinline__ float unscale(float v, uint32_t b) {
     return __builtin_amdgcn_ldexpf(v, 127 - (int)b);

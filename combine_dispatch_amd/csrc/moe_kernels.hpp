@@ -31,9 +31,9 @@ struct MTile {
 };
 
 // Block scales in "packed k-major" layout: one 4-byte word holds the UE8M0
-// bytes of 4 consecutive 32-wide k-blocks (one 128-wide K step), byte b =
-// k-block 4*w + b, and the words of one K step are stored contiguously over
-// rows: word (w, row) at byte 4 * (w * rows_total + row).
+// bytes of the 4 consecutive 32-wide k-blocks of one 128-wide K step w, in
+// byte order (4w, 4w+2, 4w+1, 4w+3), and the words of one K step are stored
+// contiguously over rows: word (w, row) at byte 4 * (w * rows_total + row).
 struct GemmArgs {
     const uint8_t* A;    // e4m3 [rows][Kdim]
     const uint8_t* SA;   // packed k-major words [Kdim/128][cap rows]

@@ -208,8 +208,9 @@ __global__ __launch_bounds__(256) void k_dispatch_fp8(const uint16_t* __restrict
     }
 }
 
-// Pool scales in packed k-major words (the layout the GEMM loads per K step):
-// word (w, r) = word w of token pool_src[r] / K's scale row.  Thread per
+// Pool scales in packed k-major words (the layout the GEMM loads per K step,
+// bytes in the order 0, 2, 1, 3): word (w, r) = word w of token
+// pool_src[r] / K's scale row.  Thread per
 // (pool row, word); consecutive threads write consecutive rows.  Rows from R
 // on are left as they are.
 __global__ __launch_bounds__(256) void k_pool_scales(const uint32_t* __restrict__ tok_s, int W,
@@ -221,11 +222,11 @@ __global__ __launch_bounds__(256) void k_pool_scales(const uint32_t* __restrict_
     const int w = blockIdx.y;
     if (r >= offsets[E]) return;
     const int64_t t = pool_src[r] / K;
-    pool_s[(int64_t)w * cap + r] = tok_s[t * W + w];
+    pool_s[(int64_t)w * cap + r] = swap_bytes12(tok_s[t * W + w]);
 }
 
 // Weight scales [E][N][W words] (row-major, W = Kdim/128 words of 4 UE8M0
-// bytes per row) -> packed k-major [E][W][N].  Block (n-tile of 64 rows,
+// bytes per row) -> packed k-major [E][W][N], bytes in the order 0, 2, 1, 3.  Block (n-tile of 64 rows,
 // expert, word tile of 64): coalesced row reads into an LDS tile, coalesced
 // column writes out of it.
 __global__ __launch_bounds__(256) void k_scales_kmajor(const uint32_t* __restrict__ S,
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(256) void k_scales_kmajor(const uint32_t* __restric
     uint32_t* dst = St + ((int64_t)e * W + w0) * N + n0;
     for (int i = threadIdx.x; i < 64 * 64; i += 256) {
         const int w = i >> 6, r = i & 63;
-        if (w < nw) dst[(int64_t)w * N + r] = tile[w][r];
+        if (w < nw) dst[(int64_t)w * N + r] = swap_bytes12(tile[w][r]);
     }
 }
 

@@ -156,10 +156,10 @@ int moe_combine(const moe_shape_t* s, const void* pool_out, const int32_t* slot_
  * tests can read them after a call (all -1 on a bad shape). */
 /* The block scales of the pool and of the activation are stored as packed
  * k-major words: the word for row r and K step w (128 columns) holds the
- * UE8M0 bytes of the row's 32-column groups 4w..4w+3 (byte b = group 4w+b)
- * at byte offset 4 * (w * cap + r), so one K step of a row tile is one
- * contiguous run (the pages' SF buffers pack 4 UE8M0 per 128 columns, [P3]
- * appendix A.1). */
+ * UE8M0 bytes of the row's 32-column groups 4w, 4w+2, 4w+1, 4w+3 (in that
+ * byte order) at byte offset 4 * (w * cap + r), so one K step of a row tile
+ * is one contiguous run (the pages' SF buffers pack 4 UE8M0 per 128
+ * columns, [P3] appendix A.1). */
 typedef struct {
     int64_t counts, offsets, pool_src, slot_to_pool, pool_w; /* routing arrays */
     int64_t pool_q, pool_s;   /* e4m3 [cap][H], packed k-major words [H/128][cap] */

@@ -54,10 +54,11 @@ def view(workspace: torch.Tensor, inp: dict, name: str, rows: int | None = None)
     dt, shape = spec[name]
     off = v[name]
     if name in ("pool_s", "act_s"):
-        # packed k-major words: word (w, r) at 4 * (w * cap + r), byte b = group 4w + b
+        # packed k-major words: word (w, r) at 4 * (w * cap + r), bytes = groups
+        # 4w, 4w+2, 4w+1, 4w+3
         cap, groups = v["capacity_rows"], shape[1]
         raw = workspace[off:off + cap * groups].cpu().numpy()
-        rm = raw.reshape(groups // 4, cap, 4).transpose(1, 0, 2).reshape(cap, groups)
+        rm = raw.reshape(groups // 4, cap, 4)[:, :, [0, 2, 1, 3]].transpose(1, 0, 2).reshape(cap, groups)
         return np.ascontiguousarray(rm[:(rows if rows is not None else shape[0])])
     if rows is not None:
         shape = (rows,) + shape[1:]
