@@ -258,7 +258,7 @@ int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void
     hipLaunchKernelGGL(k_dispatch_fp8, dim3(T), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(x), H, K, slot_to_pool, pool_q,
                        static_cast<uint8_t*>(nullptr), tok_s);
-    hipLaunchKernelGGL(k_pool_scales, dim3((unsigned)((L.cap + 255) / 256), H / 128), dim3(256), 0,
+    hipLaunchKernelGGL(k_pool_scales, dim3((unsigned)((L.cap + 255) / 256)), dim3(256), 0,
                        stream, reinterpret_cast<const uint32_t*>(tok_s), H / 128, pool_src, offsets,
                        s->E, K, (int64_t)L.cap, reinterpret_cast<uint32_t*>(pool_s));
     prof_mark(pc, MOE_STAGE_DISPATCH, stream);

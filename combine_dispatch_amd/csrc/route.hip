@@ -210,40 +210,70 @@ __global__ __launch_bounds__(256) void k_dispatch_fp8(const uint16_t* __restrict
 
 // Pool scales in packed k-major words (the layout the GEMM loads per K step,
 // bytes in the order 0, 2, 1, 3): word (w, r) = word w of token
-// pool_src[r] / K's scale row.  Thread per
-// (pool row, word); consecutive threads write consecutive rows.  Rows from R
-// on are left as they are.
+// pool_src[r] / K's scale row.  Thread per pool row: the token's row is read
+// as 16-byte pieces, and for each w consecutive threads write consecutive
+// words.  Rows from R on are left as they are.
 __global__ __launch_bounds__(256) void k_pool_scales(const uint32_t* __restrict__ tok_s, int W,
                                                     const int32_t* __restrict__ pool_src,
                                                     const int32_t* __restrict__ offsets, int E,
                                                     int K, int64_t cap,
                                                     uint32_t* __restrict__ pool_s) {
     const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int w = blockIdx.y;
     if (r >= offsets[E]) return;
     const int64_t t = pool_src[r] / K;
-    pool_s[(int64_t)w * cap + r] = swap_bytes12(tok_s[t * W + w]);
+    if ((W & 3) == 0) {
+        const uint4* src = reinterpret_cast<const uint4*>(tok_s + t * W);
+        for (int w4 = 0; w4 < W / 4; ++w4) {
+            const uint4 v = src[w4];
+            pool_s[(int64_t)(4 * w4 + 0) * cap + r] = swap_bytes12(v.x);
+            pool_s[(int64_t)(4 * w4 + 1) * cap + r] = swap_bytes12(v.y);
+            pool_s[(int64_t)(4 * w4 + 2) * cap + r] = swap_bytes12(v.z);
+            pool_s[(int64_t)(4 * w4 + 3) * cap + r] = swap_bytes12(v.w);
+        }
+    } else {
+        for (int w = 0; w < W; ++w) pool_s[(int64_t)w * cap + r] = swap_bytes12(tok_s[t * W + w]);
+    }
 }
 
 // Weight scales [E][N][W words] (row-major, W = Kdim/128 words of 4 UE8M0
-// bytes per row) -> packed k-major [E][W][N], bytes in the order 0, 2, 1, 3.  Block (n-tile of 64 rows,
-// expert, word tile of 64): coalesced row reads into an LDS tile, coalesced
-// column writes out of it.
+// bytes per row) -> packed k-major [E][W][N], bytes in the order 0, 2, 1, 3.
+// Block (n-tile of 64 rows, expert, word tile of 64): 16-byte row reads into
+// an LDS tile, 16-byte column writes (4 rows of one word) out of it.
 __global__ __launch_bounds__(256) void k_scales_kmajor(const uint32_t* __restrict__ S,
                                                       uint32_t* __restrict__ St, int N, int W) {
-    __shared__ uint32_t tile[64][65];
+    __shared__ uint32_t tile[64][64 + 4];
     const int n0 = blockIdx.x * 64, e = blockIdx.y, w0 = blockIdx.z * 64;
     const int nw = min(64, W - w0);
     const uint32_t* src = S + ((int64_t)e * N + n0) * W + w0;
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-        const int r = i >> 6, w = i & 63;
-        if (w < nw) tile[w][r] = src[(int64_t)r * W + w];
+    if ((W & 3) == 0) {  // rows are 16-byte aligned
+        for (int i = threadIdx.x; i < 64 * 16; i += 256) {
+            const int r = i >> 4, w4 = i & 15;
+            if (4 * w4 < nw) {
+                const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)r * W + 4 * w4);
+                tile[4 * w4 + 0][r] = v.x;
+                tile[4 * w4 + 1][r] = v.y;
+                tile[4 * w4 + 2][r] = v.z;
+                tile[4 * w4 + 3][r] = v.w;
+            }
+        }
+    } else {
+        for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+            const int r = i >> 6, w = i & 63;
+            if (w < nw) tile[w][r] = src[(int64_t)r * W + w];
+        }
     }
     __syncthreads();
     uint32_t* dst = St + ((int64_t)e * W + w0) * N + n0;
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-        const int w = i >> 6, r = i & 63;
-        if (w < nw) dst[(int64_t)w * N + r] = swap_bytes12(tile[w][r]);
+    for (int i = threadIdx.x; i < 64 * 16; i += 256) {
+        const int w = i >> 4, r4 = i & 15;
+        if (w < nw) {
+            uint4 v;
+            v.x = swap_bytes12(tile[w][4 * r4 + 0]);
+            v.y = swap_bytes12(tile[w][4 * r4 + 1]);
+            v.z = swap_bytes12(tile[w][4 * r4 + 2]);
+            v.w = swap_bytes12(tile[w][4 * r4 + 3]);
+            *reinterpret_cast<uint4*>(dst + (int64_t)w * N + 4 * r4) = v;
+        }
     }
 }
 
