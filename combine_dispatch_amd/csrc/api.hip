@@ -129,7 +129,7 @@ int run_routing(const moe_shape_t* s, const Layout& L, const int64_t* topk_idx, 
     hipLaunchKernelGGL(k_route_count, dim3(nblk), dim3(kRouteThreads), lds, stream, topk_idx, TK,
                        E, seg_hist, seg_err);
     prof_mark(pc, MOE_STAGE_ROUTE_COUNT, stream);
-    const int scan_threads = ((E + 63) / 64) * 64;
+    const int scan_threads = 1024;  // several threads per expert split the segments
     hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(scan_threads), 0, stream, seg_hist, seg_err,
                        (int)L.nseg, E, seg_base, counts, offsets,
                        reinterpret_cast<MTile*>(ws + L.mtiles),
@@ -323,7 +323,7 @@ int moe_dispatch(const moe_shape_t* s, const void* x, const int64_t* topk_idx, c
         // offsets = 0
         if (!device_ok()) return MOE_ERR_DEVICE;
         uint8_t* ws = static_cast<uint8_t*>(workspace);
-        const int scan_threads = ((s->E + 63) / 64) * 64;
+        const int scan_threads = 1024;
         hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(scan_threads), 0, stream,
                            reinterpret_cast<int32_t*>(ws + L.seg_hist),
                            reinterpret_cast<int32_t*>(ws + L.seg_err), 0, s->E,

@@ -52,27 +52,51 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_count(
     }
 }
 
-// a2: exclusive prefix sum.  One block, thread e owns expert e: it walks the
-// segments (per-segment bases inside the expert), then a block-wide scan over
-// experts gives offsets[E+1]; the same scan over ceil(count/kBM) lays out the
-// GEMM's expert-major m-tile table.
+// a2: exclusive prefix sum.  One block.  The segment histogram [nseg][E] is
+// split among P threads per expert (P a power of two, P*E <= blockDim;
+// thread tid = p*E + e, so a wave reads consecutive experts of a segment):
+// each sums its chunk of segments, the chunk sums are scanned per expert,
+// then a block-wide scan over experts gives offsets[E+1] and, over
+// ceil(count/kBM), the GEMM's expert-major m-tile table; finally each thread
+// walks its chunk again writing the per-segment bases.
 __global__ __launch_bounds__(1024) void k_route_scan(
     const int32_t* __restrict__ seg_hist, const int32_t* __restrict__ seg_err, int nseg, int E,
     int32_t* __restrict__ seg_base, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     MTile* __restrict__ mtiles, int32_t* __restrict__ num_mtiles, int32_t* __restrict__ err_flag) {
+    __shared__ int32_t s_part[1024];  // chunk sums, then chunk bases inside the expert
+    __shared__ int32_t s_cnt[1024];   // count per expert, then offset per expert
     __shared__ int32_t wsum[16], wsum_t[16], werr[16];
-    const int e = threadIdx.x;
-    const int lane = e % kWave, wv = e / kWave;
-    int run = 0, err = 0;
-    if (e < E) {
-        for (int s = 0; s < nseg; ++s) {
-            const int v = seg_hist[(int64_t)s * E + e];
-            seg_base[(int64_t)s * E + e] = run;
+    const int tid = threadIdx.x;
+    int P = 1;
+    while (2 * P * E <= (int)blockDim.x) P *= 2;
+    const int e_of = tid % E, p_of = tid / E;
+    const bool owner = p_of < P;  // tid < P*E
+    const int C = (nseg + P - 1) / P;
+    const int s0 = min(nseg, p_of * C), s1 = min(nseg, s0 + C);
+    if (owner) {
+        int sum = 0;
+#pragma unroll 8
+        for (int sg = s0; sg < s1; ++sg) sum += seg_hist[(int64_t)sg * E + e_of];
+        s_part[tid] = sum;
+    }
+    int err = 0;
+    for (int sg = tid; sg < nseg; sg += blockDim.x) err |= seg_err[sg];
+    __syncthreads();
+    if (tid < E) {
+        int run = 0;
+        for (int q = 0; q < P; ++q) {
+            const int v = s_part[q * E + tid];
+            s_part[q * E + tid] = run;
             run += v;
         }
+        s_cnt[tid] = run;
     }
-    for (int s = e; s < nseg; s += blockDim.x) err |= seg_err[s];
-    const int cnt = e < E ? run : 0;
+    __syncthreads();
+
+    // scan over experts: thread e (< E) owns expert e
+    const int e = tid;
+    const int lane = e % kWave, wv = e / kWave;
+    const int cnt = e < E ? s_cnt[e] : 0;
     const int nt = (cnt + kBM - 1) / kBM;
     int inc = cnt, inc_t = nt;
     for (int d = 1; d < kWave; d <<= 1) {
@@ -102,7 +126,6 @@ __global__ __launch_bounds__(1024) void k_route_scan(
     if (e < E) {
         counts[e] = cnt;
         offsets[e] = off;
-        for (int s = 0; s < nseg; ++s) seg_base[(int64_t)s * E + e] += off;
         for (int i = 0; i < nt; ++i) {
             MTile m;
             m.expert = e;
@@ -116,6 +139,19 @@ __global__ __launch_bounds__(1024) void k_route_scan(
         offsets[E] = off + cnt;
         *num_mtiles = toff + nt;
         *err_flag = any_err;
+    }
+    __syncthreads();  // s_cnt now read as counts by every owner below
+    if (e < E) s_cnt[e] = off;
+    __syncthreads();
+    if (owner) {
+        int run = s_cnt[e_of] + s_part[tid];
+#pragma unroll 8
+        for (int sg = s0; sg < s1; ++sg) {
+            const int64_t i = (int64_t)sg * E + e_of;
+            const int v = seg_hist[i];
+            seg_base[i] = run;
+            run += v;
+        }
     }
 }
 
