@@ -244,7 +244,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     // split into the pieces read next to each MFMA, in the order the next
     // sub-step's MFMAs (row tile 0 with column tiles 0..7, then row tile 1)
     // consume them: row tile 0, the column tiles, row tile 1.
-    auto read_piece = [&](SubFrags& f, const uint8_t* base, int s, int g) __attribute__((always_inline)) {
+    // ACT (0..2): how many of the wave's two row tiles hold rows of the tile
+    // (a short last tile of an expert leaves some waves with none); reads and
+    // MFMAs of the other row tiles are skipped.
+    auto read_piece = [&](SubFrags& f, const uint8_t* base, int s, int g, auto act) __attribute__((always_inline)) {
+        constexpr int ACT = decltype(act)::value;
+        if (ACT == 0) return;
         const uint8_t* sA = base;
         const uint8_t* sB = base + kStageA;
         auto read_a = [&](int i, int part) __attribute__((always_inline)) {
@@ -264,7 +269,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
             const uint4 v = *reinterpret_cast<const uint4*>(rowp + 16 * ((2 * s + h) ^ b_sw));
             f.b[j] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
         } else if (g < 12) {
-            read_a(1, g - 10);
+            if (ACT > 1) read_a(1, g - 10);
         }
     };
     // Scale words of a step: part 0 the two A words (8 bytes), parts 1 and 2
@@ -281,15 +286,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
             w.b[j0] = (int)v.x; w.b[j0 + 1] = (int)v.y; w.b[j0 + 2] = (int)v.z; w.b[j0 + 3] = (int)v.w;
         }
     };
-    auto read_all = [&](SubFrags& f, ScaleWords& w, const uint8_t* base, int s) __attribute__((always_inline)) {
+    auto read_all = [&](SubFrags& f, ScaleWords& w, const uint8_t* base, int s, auto act) __attribute__((always_inline)) {
+        if (decltype(act)::value == 0) return;
 #pragma unroll
-        for (int g = 0; g < 12; ++g) read_piece(f, base, s, g);
+        for (int g = 0; g < 12; ++g) read_piece(f, base, s, g, act);
 #pragma unroll
         for (int part = 0; part < 3; ++part) read_scales(w, base, part);
     };
     // Scale words read beside the pieces of the next step's sub-step 0.
-    auto read_piece_and_scales = [&](SubFrags& f, ScaleWords& w, const uint8_t* base, int g) __attribute__((always_inline)) {
-        read_piece(f, base, 0, g);
+    auto read_piece_and_scales = [&](SubFrags& f, ScaleWords& w, const uint8_t* base, int g, auto act) __attribute__((always_inline)) {
+        if (decltype(act)::value == 0) return;
+        read_piece(f, base, 0, g, act);
         if (g == 0) read_scales(w, base, 0);
         if (g == 1) read_scales(w, base, 1);
         if (g == 5) read_scales(w, base, 2);
@@ -297,16 +304,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     // Words as read -> words the MFMAs use (see ScaleWords); done beside the
     // first MFMA that needs each.
     const int hs = 16 * h;
-    auto shift_for = [&](ScaleWords& c, const ScaleWords& n, int g) __attribute__((always_inline)) {
+    auto shift_for = [&](ScaleWords& c, const ScaleWords& n, int g, auto act) __attribute__((always_inline)) {
+        if (decltype(act)::value == 0) return;
         if (g == 0) { c.a[0] = (int)((uint32_t)n.a[0] >> hs); c.b[0] = (int)((uint32_t)n.b[0] >> hs); }
         if (g > 0 && g < 8) c.b[g] = (int)((uint32_t)n.b[g] >> hs);
         if (g == 8) c.a[1] = (int)((uint32_t)n.a[1] >> hs);
     };
     // MFMA number g (0..15) of sub-step S: row tile g/8, column tile g%8;
     // scale byte S of the words.
-    auto mfma_one = [&](const SubFrags& f, const ScaleWords& w, auto sub, int g) __attribute__((always_inline)) {
+    auto mfma_one = [&](const SubFrags& f, const ScaleWords& w, auto sub, int g, auto act) __attribute__((always_inline)) {
         constexpr int S = decltype(sub)::value;
         const int i = g >> 3, j = g & 7;
+        if (i >= decltype(act)::value) return;
         const v8i b = v8i{f.b[j][0], f.b[j][1], f.b[j][2], f.b[j][3], 0, 0, 0, 0};
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], b, acc[i][j], 0, 4, S,
                                                                      w.a[i], S, w.b[j]);
@@ -339,72 +348,85 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
         barrier_after_vmcnt14();
     else
         barrier_after_vmcnt0();
-    SubFrags X, Y;
-    ScaleWords Wc, Wn;  // words in use (shifted), words of the next step as read
-    read_all(X, Wn, st0, 0);
-    const uint8_t* cur = st0;
-    const uint8_t* next = st1;
-    const uint8_t* third = st2;
-    int k = 0;
-    for (; k + 3 < nk; ++k) {
-        const uint32_t dst2 = lds_addr(third);
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-            shift_for(Wc, Wn, g);
-            mfma_one(X, Wc, sub0, g);
-            read_piece(Y, cur, 1, g);
-            issue_spread(dst2, k + 2, 1, g);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        barrier_after_vmcnt14();
-        __builtin_amdgcn_sched_barrier(0);
-        const uint32_t dst3 = lds_addr(cur);
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-            mfma_one(Y, Wc, sub1, g);
-            read_piece_and_scales(X, Wn, next, g);
-            issue_spread(dst3, k + 3, 0, g);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        const uint8_t* t = cur;
-        cur = next;
-        next = third;
-        third = t;
-    }
-    // The last min(nk, 3) steps issue no new steps.  Each is straight-line
-    // code (a branch inside would let the compiler sink MFMAs past the
-    // barrier); the first of them (when nk >= 3) sends the second half of the
-    // last step's loads, and its barrier then waits for step k+1 only.
-    auto tail_step = [&](auto issue_tag) __attribute__((always_inline)) {
-        constexpr bool kIssue = decltype(issue_tag)::value;
-        if (kIssue) issue_half(lds_addr(third), k + 2, 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-            shift_for(Wc, Wn, g);
-            mfma_one(X, Wc, sub0, g);
-            read_piece(Y, cur, 1, g);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (kIssue)
+    // The K loop, for a wave with ACT row tiles holding rows; every variant
+    // issues the same loads and meets the same barriers.
+    auto k_loop = [&](auto act) __attribute__((always_inline)) {
+        SubFrags X, Y;
+        ScaleWords Wc, Wn;  // words in use (shifted), words of the next step as read
+        read_all(X, Wn, st0, 0, act);
+        const uint8_t* cur = st0;
+        const uint8_t* next = st1;
+        const uint8_t* third = st2;
+        int k = 0;
+        for (; k + 3 < nk; ++k) {
+            const uint32_t dst2 = lds_addr(third);
+    #pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                shift_for(Wc, Wn, g, act);
+                mfma_one(X, Wc, sub0, g, act);
+                read_piece(Y, cur, 1, g, act);
+                issue_spread(dst2, k + 2, 1, g);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             barrier_after_vmcnt14();
-        else
-            barrier_after_vmcnt0();
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-            mfma_one(Y, Wc, sub1, g);
-            read_piece_and_scales(X, Wn, next, g);  // on the last step: a stale stage, unused
             __builtin_amdgcn_sched_barrier(0);
+            const uint32_t dst3 = lds_addr(cur);
+    #pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                mfma_one(Y, Wc, sub1, g, act);
+                read_piece_and_scales(X, Wn, next, g, act);
+                issue_spread(dst3, k + 3, 0, g);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const uint8_t* t = cur;
+            cur = next;
+            next = third;
+            third = t;
         }
-        const uint8_t* t = cur;
-        cur = next;
-        next = third;
-        third = t;
-        ++k;
+        // The last min(nk, 3) steps issue no new steps.  Each is straight-line
+        // code (a branch inside would let the compiler sink MFMAs past the
+        // barrier); the first of them (when nk >= 3) sends the second half of the
+        // last step's loads, and its barrier then waits for step k+1 only.
+        auto tail_step = [&](auto issue_tag) __attribute__((always_inline)) {
+            constexpr bool kIssue = decltype(issue_tag)::value;
+            if (kIssue) issue_half(lds_addr(third), k + 2, 1);
+            __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                shift_for(Wc, Wn, g, act);
+                mfma_one(X, Wc, sub0, g, act);
+                read_piece(Y, cur, 1, g, act);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (kIssue)
+                barrier_after_vmcnt14();
+            else
+                barrier_after_vmcnt0();
+            __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                mfma_one(Y, Wc, sub1, g, act);
+                read_piece_and_scales(X, Wn, next, g, act);  // on the last step: a stale stage, unused
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const uint8_t* t = cur;
+            cur = next;
+            next = third;
+            third = t;
+            ++k;
+        };
+        if (nk >= 3) tail_step(std::true_type{});
+        while (k < nk) tail_step(std::false_type{});
     };
-    if (nk >= 3) tail_step(std::true_type{});
-    while (k < nk) tail_step(std::false_type{});
+    // (L2 only: a short L1 tile is bound by its loads, and the variants cost
+    // the L1 kernel registers)
+    const int nact = MODE == kL1 ? 2 : (nrows > 64 * wm + 32 ? 2 : (nrows > 64 * wm ? 1 : 0));
+    if (nact == 2)
+        k_loop(std::integral_constant<int, 2>{});
+    else if (nact == 1)
+        k_loop(std::integral_constant<int, 1>{});
+    else
+        k_loop(std::integral_constant<int, 0>{});
     // ---- epilogue ------------------------------------------------------------
     // Register r of tile (i, j) is row 64*wm + 32*i + 8*(r/4) + 4*h + r%4;
     // thanks to the column order of the B rows each lane holds adjacent output
@@ -417,7 +439,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
         uint8_t* out_base = reinterpret_cast<uint8_t*>(g.out + (int64_t)row0 * N + nt * kBN);  // wave-uniform
         auto rows = [&](auto partial) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i) {
+                if (decltype(partial)::value && 64 * wm + 32 * i >= nrows) continue;  // no rows
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     // columns 8*l32 + j, j = 0..7: 16 bytes
@@ -430,6 +453,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
                     if (!decltype(partial)::value || lrow < nrows)
                         *reinterpret_cast<uint4*>(out_base + (uint32_t)(2 * (lrow * N + 8 * l32))) = v;
                 }
+            }
         };
         rows(std::true_type{});
     } else {
@@ -450,7 +474,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
         auto rows = [&](auto fast, auto partial) __attribute__((always_inline)) {
             constexpr bool kPartial = decltype(partial)::value;
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i) {
+                if (kPartial && 64 * wm + 32 * i >= nrows) continue;  // no rows
 #pragma unroll
                 for (int rq = 0; rq < 4; ++rq) {
                     const int lrow0 = 64 * wm + 32 * i + 8 * rq + 4 * h;
@@ -495,6 +520,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
                     if (rsel < 4 && (!kPartial || lrow0 + rsel < nrows))
                         s_base[(uint32_t)((lrow0 + rsel) * 4 + gbyte)] = (uint8_t)bsel;
                 }
+            }
         };
         if (g.fast_math)
             rows(std::true_type{}, std::true_type{});
