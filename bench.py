@@ -143,6 +143,18 @@ def main():
     stage_ms, ncalls = moe.moe_profile_stop()
     per_launch = {k: v / max(ncalls, 1) for k, v in stage_ms.items()}
 
+    # one more step with cold caches: a 512 MiB scrub (twice the 256 MB
+    # infinity cache) right before it; reported beside the warm number
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    scrub.fill_(3)
+    ec0, ec1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ec0.record(stream)
+    step()
+    ec1.record(stream)
+    torch.cuda.synchronize()
+    cold_ms = ec0.elapsed_time(ec1)
+    del scrub
+
     if a.copy_mib > 0:
         n = a.copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -193,6 +205,7 @@ def main():
             "combine_gbs": round(comb_bytes / (per_launch["combine"] * 1e-3) / 1e9, 1),
             "hbm_peak_gbs": PEAK_HBM_GBS,
         },
+        "cold_ms_per_step": round(cold_ms, 4),
         "wall_s_timed": round(wall, 4),
         "input_gen_s": round(gen_s, 2),
     }
