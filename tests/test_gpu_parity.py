@@ -51,13 +51,22 @@ def check_routing(inp, ws):
 
 
 def check_act(gq, gs, rq, rs):
-    """FP8 intermediate: codes [n][I], scale bytes [n][I/32]."""
+    """FP8 intermediate: codes [n][I], scale bytes [n][I/32].
+
+    At most CODE_FRAC of the codes may differ, each by one e4m3 step; near
+    zero (both codes subnormal) by two subnormal steps, i.e. 2^-8 of the
+    group scale.  The scaled MFMA does not accumulate a 64-wide K block
+    exactly in fp32 (measured: a block whose exact sum has 22 significant
+    bits comes out 2^-18 off), so an activation whose exact value is 0 can
+    come out a step or two of the subnormal grid away from 0."""
     sdiff = np.abs(gs.astype(np.int32) - rs.astype(np.int32))
     assert sdiff.max(initial=0) <= 1
     assert (sdiff != 0).mean() <= CODE_FRAC
     same = np.repeat(sdiff == 0, 32, axis=1)
     dist = e4m3_step_distance(gq, rq)
-    assert dist[same].max(initial=0) <= 1
+    subnormal = ((gq & 0x78) == 0) & ((rq & 0x78) == 0)
+    allowed = np.where(subnormal, 2, 1)
+    assert (dist[same] <= allowed[same]).all(), dist[same].max(initial=0)
     assert (dist[same] != 0).mean() <= CODE_FRAC, (dist[same] != 0).mean()
     if (~same).any():  # scale moved by one step: values within one step of the coarser scale
         gv = oracle.e4m3_to_f32(gq) * np.exp2(np.repeat(gs, 32, axis=1).astype(np.float64) - 127)
@@ -87,6 +96,10 @@ SMALL = [
     dict(T=71, H=768, I=384, E=40, K=4, routing="zipf", seed=43, zipf_s=2.0, mask_p=0.05),
     # every slot of some tokens masked
     dict(T=64, H=256, I=128, E=4, K=2, routing="uniform", seed=44, mask_p=0.6),
+    # the largest expert count (one scan thread per expert), most experts empty
+    dict(T=200, H=256, I=128, E=1000, K=8, routing="zipf", seed=45, mask_p=0.02),
+    # an expert count that is not a power of two (two scan threads per expert)
+    dict(T=150, H=512, I=256, E=257, K=6, routing="uniform", seed=46),
 ]
 
 
@@ -96,7 +109,8 @@ def small_inputs(case):
     return moe_inputs.make_inputs(**case)
 
 
-@pytest.mark.parametrize("case", SMALL, ids=["tiny", "ragged", "dense", "sparse", "masked"])
+@pytest.mark.parametrize("case", SMALL, ids=["tiny", "ragged", "dense", "sparse", "masked",
+                                             "e1000", "e257"])
 def test_forward_matches_oracle_small(case):
     inp = small_inputs(case)
     say("case", case)
