@@ -444,11 +444,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     // columns 8*l32 + j, j = 0..7: 16 bytes
+                    float c[8];  // read from the accumulator registers where used
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) asm("v_accvgpr_read_b32 %0, %1" : "=v"(c[j]) : "a"(acc[i][j][r]));
                     uint4 v;
-                    v.x = pack_bf16x2(acc[i][0][r], acc[i][1][r]);
-                    v.y = pack_bf16x2(acc[i][2][r], acc[i][3][r]);
-                    v.z = pack_bf16x2(acc[i][4][r], acc[i][5][r]);
-                    v.w = pack_bf16x2(acc[i][6][r], acc[i][7][r]);
+                    v.x = pack_bf16x2(c[0], c[1]);
+                    v.y = pack_bf16x2(c[2], c[3]);
+                    v.z = pack_bf16x2(c[4], c[5]);
+                    v.w = pack_bf16x2(c[6], c[7]);
                     const int lrow = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
                     if (!decltype(partial)::value || lrow < nrows)
                         *reinterpret_cast<uint4*>(out_base + (uint32_t)(2 * (lrow * N + 8 * l32))) = v;
@@ -489,7 +492,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj) {
                             // gate and up rounded to bf16 by one conversion
-                            const uint32_t gu = pack_bf16x2(acc[i][jj][r], acc[i][jj + 4][r]);
+                            // read from the accumulator registers where used (else the
+                            // compiler copies all 256 up front and runs out of
+                            // registers for independent chains)
+                            float ga, ua;
+                            asm("v_accvgpr_read_b32 %0, %1" : "=v"(ga) : "a"(acc[i][jj][r]));
+                            asm("v_accvgpr_read_b32 %0, %1" : "=v"(ua) : "a"(acc[i][jj + 4][r]));
+                            const uint32_t gu = pack_bf16x2(ga, ua);
                             const float gt = bf16_lo(gu), up = bf16_hi(gu);
                             float sl;
                             if (decltype(fast)::value) {
