@@ -181,9 +181,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     // b_row its expert rows differ from those of load 0 by a wave-uniform
     // number of rows, which goes into the scalar base.
     const uint32_t b_off = (uint32_t)((b_row<MODE>(nt, (tid >> 2), g.I) - b_r0) * b_ld + 16 * b_chunk);
-    const int b_dq1 = b_row<MODE>(0, 64, g.I) - b_row<MODE>(0, 0, g.I);
-    const int b_dq2 = b_row<MODE>(0, 128, g.I) - b_row<MODE>(0, 0, g.I);
-    const int b_dq3 = b_row<MODE>(0, 192, g.I) - b_row<MODE>(0, 0, g.I);
+    // per-load lane offsets (in vector registers: the scalar registers hold
+    // one base per operand, advanced by K each step)
+    const uint32_t a_off0 = a_off, a_off1 = a_off + 32 * Kdim, a_off2 = a_off + 64 * Kdim,
+                   a_off3 = a_off + 96 * Kdim, a_off4 = a_off + 128 * Kdim, a_off5 = a_off + 160 * Kdim,
+                   a_off6 = a_off + 192 * Kdim, a_off7 = a_off + 224 * Kdim;
+    const uint32_t b_off0 = b_off,
+                   b_off1 = b_off + (b_row<MODE>(0, 64, g.I) - b_row<MODE>(0, 0, g.I)) * b_ld,
+                   b_off2 = b_off + (b_row<MODE>(0, 128, g.I) - b_row<MODE>(0, 0, g.I)) * b_ld,
+                   b_off3 = b_off + (b_row<MODE>(0, 192, g.I) - b_row<MODE>(0, 0, g.I)) * b_ld;
     // scales: packed k-major words, one 4-byte word (4 k-blocks) per row per
     // step, the words of a step contiguous over rows.  LDS word p of the A
     // scales is row tile p%2 of wave p/64, lane row (p%64)/2, so a lane's two
@@ -206,10 +212,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     auto issue_piece = [&](uint32_t st, int kk, int g) __attribute__((always_inline)) {
         const int k0 = kk * kBK;
         if (g < 8) {
-            dma_x4(st + w_dst16 + 4096 * g, a_base + k0 + (int64_t)g * 32 * Kdim, a_off);
+            const uint32_t off = g == 0 ? a_off0 : g == 1 ? a_off1 : g == 2 ? a_off2 : g == 3 ? a_off3
+                               : g == 4 ? a_off4 : g == 5 ? a_off5 : g == 6 ? a_off6 : a_off7;
+            dma_x4(st + w_dst16 + 4096 * g, a_base + k0, off);
         } else if (g < 12) {
-            const int dq = g == 8 ? 0 : g == 9 ? b_dq1 : g == 10 ? b_dq2 : b_dq3;
-            dma_x4(st + kStageA + w_dst16 + 4096 * (g - 8), b_base + k0 / 2 + (int64_t)dq * b_ld, b_off);
+            const uint32_t off = g == 8 ? b_off0 : g == 9 ? b_off1 : g == 10 ? b_off2 : b_off3;
+            dma_x4(st + kStageA + w_dst16 + 4096 * (g - 8), b_base + k0 / 2, off);
         } else if (g == 12) {
             dma_x1(st + kStageA + kStageB + w_dst4, sa_base + kk * sa_step, sa_off);
         } else if (g == 13) {
