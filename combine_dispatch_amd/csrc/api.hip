@@ -85,6 +85,25 @@ int device_ok() {
     return ok;
 }
 
+// Workgroups of a persistent GEMM launch: one per CU (at most one fits, by
+// LDS), a multiple of 8 so that every XCD gets the same number, and no more
+// than there can be tiles.
+unsigned gemm_grid(int64_t max_tiles) {
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    int n = dev < 64 ? cus[dev] : 0;
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+            n = 8;
+        if (dev < 64) cus[dev] = n;
+    }
+    int64_t w = n / 8 * 8;
+    const int64_t need = (max_tiles + 7) / 8 * 8;
+    if (need < w) w = need;
+    return (unsigned)(w < 8 ? 8 : w);
+}
+
 int launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
 // ---- optional per-kernel timing (moe_profile.h) ------------------------------
@@ -280,8 +299,8 @@ int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void
     g1.act_s = act_s;
     g1.I = I;
     g1.fast_math = o.fast_math ? 1 : 0;
-    hipLaunchKernelGGL(k_gemm_l1, dim3((unsigned)(L.max_mtiles * g1.ntiles)), dim3(kGemmThreads),
-                       0, stream, g1);
+    hipLaunchKernelGGL(k_gemm_l1, dim3(gemm_grid(L.max_mtiles * g1.ntiles)), dim3(kGemmThreads), 0,
+                       stream, g1);
     prof_mark(pc, MOE_STAGE_GEMM_L1, stream);
 
     GemmArgs g2 = g1;
@@ -293,8 +312,8 @@ int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void
     g2.N = H;
     g2.ntiles = H / kBN;
     g2.out = l2_out;
-    hipLaunchKernelGGL(k_gemm_l2, dim3((unsigned)(L.max_mtiles * g2.ntiles)), dim3(kGemmThreads),
-                       0, stream, g2);
+    hipLaunchKernelGGL(k_gemm_l2, dim3(gemm_grid(L.max_mtiles * g2.ntiles)), dim3(kGemmThreads), 0,
+                       stream, g2);
     prof_mark(pc, MOE_STAGE_GEMM_L2, stream);
 
     hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, stream, l2_out, slot_to_pool,

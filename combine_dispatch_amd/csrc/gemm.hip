@@ -64,14 +64,6 @@ __device__ __forceinline__ int b_row(int nt, int nrow, int I) {
     return nt * kBN + 8 * c + j;
 }
 
-__device__ __forceinline__ int tile_of_block(int bid, int nblk) {
-    // Hardware hands out workgroups round-robin over 8 XCDs; give XCD x a
-    // contiguous range of logical tiles instead.
-    const int per = nblk / 8, rem = nblk % 8;
-    const int xcd = bid % 8, j = bid / 8;
-    return xcd * per + min(xcd, rem) + j;
-}
-
 // MFMA operands of one 64-wide K sub-step for one wave: A fragments of its 2
 // row tiles, B fragments of the 8 column tiles.
 struct SubFrags {
@@ -130,35 +122,63 @@ __device__ __forceinline__ void barrier_after_vmcnt21() {
 __device__ __forceinline__ void barrier_after_vmcnt0() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// Every wave's LDS reads are done (the stages may be overwritten).
+__device__ __forceinline__ void lds_reads_done_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// A copy of v that the compiler cannot compute before this point: keeps the
+// epilogue's per-lane address arithmetic (the same for every tile) from being
+// hoisted out of the tile loop, where it would hold registers across the K
+// loop.
+__device__ __forceinline__ int late_copy(int v) {
+    int r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
 
 // One LDS stage: A tile [256 rows][128 B], B tile [256 rows][64 B], then one
-// dword of scale bytes per A row and per B row.
+// kilobyte of A scale words and one of B scale words.
+//
+// Persistent: one workgroup per CU loops over tiles.  The grid is a multiple
+// of 8 and the hardware places workgroup b on XCD b % 8; XCD x owns the
+// logical tiles [total*x/8, total*(x+1)/8) and its workgroups take them
+// round-robin, so the ~32 workgroups of an XCD work on consecutive tiles of
+// one group and share both operands through that XCD's L2.  After a tile's K
+// loop the first loads of the next tile go out before the epilogue, so their
+// latency (and the launch of a new workgroup) hide behind it.
 template <int MODE>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8_t* st1,
-                                          uint8_t* st2, float* s_w) {
+__device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0, uint8_t* st1,
+                                                uint8_t* st2, float* s_wa, float* s_wb) {
     const int tid = threadIdx.x;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63;
     const int wm = wid;  // rows 64*wm .. 64*wm+63 of the tile, all 256 columns
     const int h = lane >> 5, l32 = lane & 31;
 
-    // Tile order: groups of kGroupM m-tiles x all n-tiles, m fastest, so the
-    // ~32 workgroups an XCD runs at once cover 4 m-tiles x 8 n-tiles and
-    // share both operands through that XCD's L2.
-    const int logical = tile_of_block(blockIdx.x, gridDim.x);
-    const int num_m = *g.num_mtiles;
-    if (logical >= num_m * g.ntiles) return;
-    const int group = logical / (kGroupM * g.ntiles);
-    const int in_group = logical - group * (kGroupM * g.ntiles);
-    const int gm = min(kGroupM, num_m - group * kGroupM);
-    const int mt = group * kGroupM + in_group % gm;
-    const int nt = in_group / gm;
-    const MTile tile = g.mtiles[mt];
-    const int e = tile.expert, row0 = tile.row0, nrows = tile.nrows;
     const int Kdim = g.Kdim;
     const int nk = Kdim / kBK;
 
-    if (MODE == kL1) s_w[tid] = tid < nrows ? g.pool_w[row0 + tid] : 0.f;
+    // Tile order: groups of kGroupM m-tiles x all n-tiles, m fastest, so the
+    // ~32 workgroups of an XCD cover 4 m-tiles x 8 n-tiles at a time.
+    const int num_m = *g.num_mtiles;
+    const int total = num_m * g.ntiles;
+    const int xcd = blockIdx.x & 7, nj = (int)gridDim.x >> 3;
+    const int t_hi = (int)((int64_t)total * (xcd + 1) / 8);
+    int logical = (int)((int64_t)total * xcd / 8) + (int)(blockIdx.x >> 3);
+    if (logical >= t_hi) return;
+    int e = 0, row0 = 0, nrows = 0, nt = 0;
+    auto decode = [&](int lg) __attribute__((always_inline)) {
+        const int group = lg / (kGroupM * g.ntiles);
+        const int in_group = lg - group * (kGroupM * g.ntiles);
+        const int gm = min(kGroupM, num_m - group * kGroupM);
+        const int mt = group * kGroupM + in_group % gm;
+        nt = in_group / gm;
+        const MTile tile = g.mtiles[mt];
+        e = tile.expert;
+        row0 = tile.row0;
+        nrows = tile.nrows;
+    };
+    decode(logical);
 
     // ---- global -> LDS direct loads --------------------------------------
     // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS at M0 + 16 l,
@@ -170,17 +190,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     // row q/8, physical chunk q%8, holding logical chunk (q%8) ^ ((row/2)%8).
     const int a_chunk = (tid & 7) ^ ((tid >> 4) & 7);
     const uint32_t a_off = (uint32_t)((tid >> 3) * Kdim + 16 * a_chunk);
-    const uint8_t* a_base = g.A + (int64_t)row0 * Kdim;
     // B: 1024 chunks; chunk q = tid + 256 i is LDS row q/4 (B row b_row(q/4)),
     // physical chunk q%4, logical chunk (q%4) ^ ((row/4)%4).
     const int b_chunk = (tid & 3) ^ ((tid >> 4) & 3);
     const int b_ld = Kdim / 2;
-    const int b_r0 = b_row<MODE>(nt, 0, g.I);
-    const uint8_t* b_base = g.B + ((int64_t)e * g.N + b_r0) * b_ld;
     // Load q (0..3) covers LDS B rows 64q + tid/4; with the column order of
     // b_row its expert rows differ from those of load 0 by a wave-uniform
     // number of rows, which goes into the scalar base.
-    const uint32_t b_off = (uint32_t)((b_row<MODE>(nt, (tid >> 2), g.I) - b_r0) * b_ld + 16 * b_chunk);
+    // (row offsets relative to the tile's first B row do not depend on the tile)
+    const uint32_t b_off = (uint32_t)((b_row<MODE>(0, (tid >> 2), g.I) - b_row<MODE>(0, 0, g.I)) * b_ld + 16 * b_chunk);
     // per-load lane offsets (in vector registers: the scalar registers hold
     // one base per operand, advanced by K each step)
     const uint32_t a_off0 = a_off, a_off1 = a_off + 32 * Kdim, a_off2 = a_off + 64 * Kdim,
@@ -196,12 +214,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     // words are adjacent; LDS word p of the B scales is column tile p%8,
     // lane column p/8, so a lane's eight words are adjacent.  Thread tid loads
     // LDS word tid of each, so it picks its source row accordingly.
-    const uint8_t* sa_base = g.SA + (int64_t)row0 * 4;
     const int64_t sa_step = g.sa_step;
     const uint32_t sa_off = (uint32_t)(4 * ((tid & ~63) + 32 * (tid & 1) + ((tid & 63) >> 1)));
     const int64_t sb_step = (int64_t)g.N * 4;
-    const uint8_t* sb_base = g.SB + (int64_t)e * (Kdim / 128) * sb_step + (int64_t)b_r0 * 4;
-    const uint32_t sb_off = (uint32_t)((b_row<MODE>(nt, 32 * (tid & 7) + (tid >> 3), g.I) - b_r0) * 4);
+    const uint32_t sb_off = (uint32_t)((b_row<MODE>(0, 32 * (tid & 7) + (tid >> 3), g.I) - b_row<MODE>(0, 0, g.I)) * 4);
+    // scalar bases of the current tile
+    const uint8_t *a_base, *b_base, *sa_base, *sb_base;
+    auto set_bases = [&]() __attribute__((always_inline)) {
+        const int b_r0 = b_row<MODE>(nt, 0, g.I);
+        a_base = g.A + (int64_t)row0 * Kdim;
+        b_base = g.B + ((int64_t)e * g.N + b_r0) * b_ld;
+        sa_base = g.SA + (int64_t)row0 * 4;
+        sb_base = g.SB + (int64_t)e * (Kdim / 128) * sb_step + (int64_t)b_r0 * 4;
+    };
+    set_bases();
     const uint32_t lds_st0 = lds_addr(st0), lds_st1 = lds_addr(st1), lds_st2 = lds_addr(st2);
     const uint32_t w_dst16 = (uint32_t)(64 * wid * 16);
     const uint32_t w_dst4 = (uint32_t)(64 * wid * 4);
@@ -234,12 +260,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     };
 
     v16f acc[2][8];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // ---- fragment reads --------------------------------------------------
     // A row of row-tile i: 64*wm + 32*i + l32, so (row/2)%8 == (l32/2)%8.
@@ -331,111 +351,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
     const std::integral_constant<int, 0> sub0;
     const std::integral_constant<int, 1> sub1;
 
-    // ---- main loop: three LDS stages, sub-step pipelined operands ---------
-    // X holds sub-step 0 and Y sub-step 1 of the current step k.  While the 16
-    // MFMAs of X run, Y is read from step k's stage and the second half of
-    // step k+2's loads goes out.  Then each wave waits for its own loads of
-    // step k+1 (the newest 14 loads may still fly) and meets the others at a
-    // barrier: step k+1's stage is complete and step k's stage is free (all
-    // its reads are done), so the first half of step k+3's loads goes into it
-    // beside the MFMAs of Y, while X is read from step k+1's stage.  Loads go
-    // out one per two MFMAs, so the load path never backs up the MFMA issue.
-    // Every MFMA is fenced together with the reads/loads issued beside it, so
-    // the compiler keeps this order; the loop body is branch-free, and the
-    // last three steps run in a second loop that issues no new steps.
-    issue_half(lds_st0, 0, 0);
-    issue_half(lds_st0, 0, 1);
-    if (nk > 1) {
-        issue_half(lds_st1, 1, 0);
-        issue_half(lds_st1, 1, 1);
-    }
-    if (nk > 2) issue_half(lds_st2, 2, 0);
-    if (nk > 2)
-        barrier_after_vmcnt21();
-    else if (nk > 1)
-        barrier_after_vmcnt14();
-    else
-        barrier_after_vmcnt0();
-    // The K loop, for a wave with ACT row tiles holding rows; every variant
-    // issues the same loads and meets the same barriers.
-    auto k_loop = [&](auto act) __attribute__((always_inline)) {
-        SubFrags X, Y;
-        ScaleWords Wc, Wn;  // words in use (shifted), words of the next step as read
-        read_all(X, Wn, st0, 0, act);
-        const uint8_t* cur = st0;
-        const uint8_t* next = st1;
-        const uint8_t* third = st2;
-        int k = 0;
-        for (; k + 3 < nk; ++k) {
-            const uint32_t dst2 = lds_addr(third);
-    #pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                shift_for(Wc, Wn, g, act);
-                mfma_one(X, Wc, sub0, g, act);
-                read_piece(Y, cur, 1, g, act);
-                issue_spread(dst2, k + 2, 1, g);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            barrier_after_vmcnt14();
-            __builtin_amdgcn_sched_barrier(0);
-            const uint32_t dst3 = lds_addr(cur);
-    #pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                mfma_one(Y, Wc, sub1, g, act);
-                read_piece_and_scales(X, Wn, next, g, act);
-                issue_spread(dst3, k + 3, 0, g);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            const uint8_t* t = cur;
-            cur = next;
-            next = third;
-            third = t;
-        }
-        // The last min(nk, 3) steps issue no new steps.  Each is straight-line
-        // code (a branch inside would let the compiler sink MFMAs past the
-        // barrier); the first of them (when nk >= 3) sends the second half of the
-        // last step's loads, and its barrier then waits for step k+1 only.
-        auto tail_step = [&](auto issue_tag) __attribute__((always_inline)) {
-            constexpr bool kIssue = decltype(issue_tag)::value;
-            if (kIssue) issue_half(lds_addr(third), k + 2, 1);
-            __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                shift_for(Wc, Wn, g, act);
-                mfma_one(X, Wc, sub0, g, act);
-                read_piece(Y, cur, 1, g, act);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (kIssue)
-                barrier_after_vmcnt14();
-            else
-                barrier_after_vmcnt0();
-            __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                mfma_one(Y, Wc, sub1, g, act);
-                read_piece_and_scales(X, Wn, next, g, act);  // on the last step: a stale stage, unused
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            const uint8_t* t = cur;
-            cur = next;
-            next = third;
-            third = t;
-            ++k;
-        };
-        if (nk >= 3) tail_step(std::true_type{});
-        while (k < nk) tail_step(std::false_type{});
-    };
-    // (L2 only: a short L1 tile is bound by its loads, and the variants cost
-    // the L1 kernel registers)
-    const int nact = MODE == kL1 ? 2 : (nrows > 64 * wm + 32 ? 2 : (nrows > 64 * wm ? 1 : 0));
-    if (nact == 2)
-        k_loop(std::integral_constant<int, 2>{});
-    else if (nact == 1)
-        k_loop(std::integral_constant<int, 1>{});
-    else
-        k_loop(std::integral_constant<int, 0>{});
+    // The epilogue of a finished tile (its row0, nrows, nt and routing weights).
+    auto epilogue = [&](const int row0, const int nrows, const int nt, const float* s_w) __attribute__((always_inline)) {
     // ---- epilogue ------------------------------------------------------------
+        const int lane = late_copy(tid & 63);
+        const int h = lane >> 5, l32 = lane & 31;
     // Register r of tile (i, j) is row 64*wm + 32*i + 8*(r/4) + 4*h + r%4;
     // thanks to the column order of the B rows each lane holds adjacent output
     // columns of that row, so rows go straight to global memory: 32 lanes
@@ -544,6 +464,154 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, uint8_t* st0, uint8
         else
             rows(std::false_type{}, std::true_type{});
     }
+    };
+
+    // ---- main loop: three LDS stages, sub-step pipelined operands ---------
+    // X holds sub-step 0 and Y sub-step 1 of the current step k.  While the 16
+    // MFMAs of X run, Y is read from step k's stage and the second half of
+    // step k+2's loads goes out.  Then each wave waits for its own loads of
+    // step k+1 (the newest 14 loads may still fly) and meets the others at a
+    // barrier: step k+1's stage is complete and step k's stage is free (all
+    // its reads are done), so the first half of step k+3's loads goes into it
+    // beside the MFMAs of Y, while X is read from step k+1's stage.  Loads go
+    // out one per two MFMAs, so the load path never backs up the MFMA issue.
+    // Every MFMA is fenced together with the reads/loads issued beside it, so
+    // the compiler keeps this order; the loop body is branch-free, and the
+    // last three steps run in a second loop that issues no new steps.
+    // First loads of a tile: its routing weights (L1), steps 0 and 1 and the
+    // first half of step 2 -- 35 loads per wave (36 with the weights).  The
+    // wait leaves the newest 21 in flight: the weights and step 0 have landed
+    // (loads complete in order; stores issued in between only make the wait
+    // longer).
+    auto prologue = [&](float* sw) __attribute__((always_inline)) {
+        if (MODE == kL1) dma_x1(lds_addr(sw) + w_dst4, g.pool_w + row0, (uint32_t)(tid * 4));
+        issue_half(lds_st0, 0, 0);
+        issue_half(lds_st0, 0, 1);
+        if (nk > 1) {
+            issue_half(lds_st1, 1, 0);
+            issue_half(lds_st1, 1, 1);
+        }
+        if (nk > 2) issue_half(lds_st2, 2, 0);
+    };
+    auto wait_prologue = [&]() __attribute__((always_inline)) {
+        if (nk > 2)
+            barrier_after_vmcnt21();
+        else if (nk > 1)
+            barrier_after_vmcnt14();
+        else
+            barrier_after_vmcnt0();
+    };
+    float* s_w = s_wa;
+    float* s_w_next = s_wb;
+    prologue(s_w);
+    wait_prologue();
+    for (;;) {
+    // The K loop, for a wave with ACT row tiles holding rows; every variant
+    // issues the same loads and meets the same barriers.
+    auto k_loop = [&](auto act) __attribute__((always_inline)) {
+        SubFrags X, Y;
+        ScaleWords Wc, Wn;  // words in use (shifted), words of the next step as read
+        read_all(X, Wn, st0, 0, act);
+        const uint8_t* cur = st0;
+        const uint8_t* next = st1;
+        const uint8_t* third = st2;
+        int k = 0;
+        for (; k + 3 < nk; ++k) {
+            const uint32_t dst2 = lds_addr(third);
+    #pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                shift_for(Wc, Wn, g, act);
+                mfma_one(X, Wc, sub0, g, act);
+                read_piece(Y, cur, 1, g, act);
+                issue_spread(dst2, k + 2, 1, g);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            barrier_after_vmcnt14();
+            __builtin_amdgcn_sched_barrier(0);
+            const uint32_t dst3 = lds_addr(cur);
+    #pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                mfma_one(Y, Wc, sub1, g, act);
+                read_piece_and_scales(X, Wn, next, g, act);
+                issue_spread(dst3, k + 3, 0, g);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const uint8_t* t = cur;
+            cur = next;
+            next = third;
+            third = t;
+        }
+        // The last min(nk, 3) steps issue no new steps.  Each is straight-line
+        // code (a branch inside would let the compiler sink MFMAs past the
+        // barrier); the first of them (when nk >= 3) sends the second half of the
+        // last step's loads, and its barrier then waits for step k+1 only.
+        auto tail_step = [&](auto issue_tag) __attribute__((always_inline)) {
+            constexpr bool kIssue = decltype(issue_tag)::value;
+            if (kIssue) issue_half(lds_addr(third), k + 2, 1);
+            __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                shift_for(Wc, Wn, g, act);
+                mfma_one(X, Wc, sub0, g, act);
+                read_piece(Y, cur, 1, g, act);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (kIssue)
+                barrier_after_vmcnt14();
+            else
+                barrier_after_vmcnt0();
+            __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                mfma_one(Y, Wc, sub1, g, act);
+                read_piece_and_scales(X, Wn, next, g, act);  // on the last step: a stale stage, unused
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const uint8_t* t = cur;
+            cur = next;
+            next = third;
+            third = t;
+            ++k;
+        };
+        if (nk >= 3) tail_step(std::true_type{});
+        while (k < nk) tail_step(std::false_type{});
+    };
+    // (L2 only: a short L1 tile is bound by its loads, and the variants cost
+    // the L1 kernel registers)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const int nact = MODE == kL1 ? 2 : (nrows > 64 * wm + 32 ? 2 : (nrows > 64 * wm ? 1 : 0));
+    if (nact == 2)
+        k_loop(std::integral_constant<int, 2>{});
+    else if (nact == 1)
+        k_loop(std::integral_constant<int, 1>{});
+    else
+        k_loop(std::integral_constant<int, 0>{});
+
+    // next tile: once every wave is done reading the stages, its first loads
+    // go out, then this tile's epilogue runs while they fly
+    const int c_row0 = row0, c_nrows = nrows, c_nt = nt;
+    const int lg_next = logical + nj;
+    const bool more = lg_next < t_hi;
+    if (more) {
+        decode(lg_next);
+        set_bases();
+        lds_reads_done_barrier();
+        prologue(s_w_next);
+    }
+    epilogue(c_row0, c_nrows, c_nt, s_w);
+    if (!more) break;
+    wait_prologue();
+    float* t = s_w;
+    s_w = s_w_next;
+    s_w_next = t;
+    logical = lg_next;
+    }
+
 }
 
 }  // namespace
@@ -552,16 +620,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_l1(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) uint8_t st0[kStageBytes];
     __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
     __shared__ __attribute__((aligned(16))) uint8_t st2[kStageBytes];
-    __shared__ float s_w[kBM];
-    gemm_tile<kL1>(args, st0, st1, st2, s_w);
+    __shared__ float s_w[2][kBM];
+    gemm_persistent<kL1>(args, st0, st1, st2, s_w[0], s_w[1]);
 }
 
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_l2(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) uint8_t st0[kStageBytes];
     __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
     __shared__ __attribute__((aligned(16))) uint8_t st2[kStageBytes];
-    __shared__ float s_w[kBM];
-    gemm_tile<kL2>(args, st0, st1, st2, s_w);
+    gemm_persistent<kL2>(args, st0, st1, st2, nullptr, nullptr);
 }
 
 }  // namespace moe
