@@ -46,6 +46,7 @@ namespace {
 
 constexpr int kL1 = 0;
 constexpr int kL2 = 1;
+constexpr int kTileCache = 256;  // tile records kept in LDS per workgroup
 constexpr int kGroupM = 4;  // m-tiles per tile-order group
 
 // Which expert-matrix row (output column) holds LDS B row `nrow` of tile nt.
@@ -148,7 +149,8 @@ __device__ __forceinline__ int late_copy(int v) {
 // latency (and the launch of a new workgroup) hide behind it.
 template <int MODE>
 __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0, uint8_t* st1,
-                                                uint8_t* st2, float* s_wa, float* s_wb) {
+                                                uint8_t* st2, float* s_wa, float* s_wb,
+                                                MTile* s_tiles) {
     const int tid = threadIdx.x;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63;
@@ -166,19 +168,31 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     const int t_hi = (int)((int64_t)total * (xcd + 1) / 8);
     int logical = (int)((int64_t)total * xcd / 8) + (int)(blockIdx.x >> 3);
     if (logical >= t_hi) return;
-    int e = 0, row0 = 0, nrows = 0, nt = 0;
-    auto decode = [&](int lg) __attribute__((always_inline)) {
+    // This workgroup's tiles, in order: the first kTileCache records
+    // {expert, row0, nrows, n-tile} are gathered into LDS once, so moving to
+    // the next tile costs an LDS read instead of a dependent global load.
+    auto record = [&](int lg) __attribute__((always_inline)) {
         const int group = lg / (kGroupM * g.ntiles);
         const int in_group = lg - group * (kGroupM * g.ntiles);
         const int gm = min(kGroupM, num_m - group * kGroupM);
-        const int mt = group * kGroupM + in_group % gm;
-        nt = in_group / gm;
-        const MTile tile = g.mtiles[mt];
-        e = tile.expert;
-        row0 = tile.row0;
-        nrows = tile.nrows;
+        MTile t = g.mtiles[group * kGroupM + in_group % gm];
+        t.pad = in_group / gm;
+        return t;
     };
-    decode(logical);
+    {
+        const int mine = (t_hi - logical + nj - 1) / nj;
+        for (int i = tid; i < min(mine, kTileCache); i += kGemmThreads) s_tiles[i] = record(logical + i * nj);
+        __syncthreads();
+    }
+    int e = 0, row0 = 0, nrows = 0, nt = 0, tile_i = 0;
+    auto decode = [&](int lg, int i) __attribute__((always_inline)) {
+        const MTile t = i < kTileCache ? s_tiles[i] : record(lg);
+        e = __builtin_amdgcn_readfirstlane(t.expert);
+        row0 = __builtin_amdgcn_readfirstlane(t.row0);
+        nrows = __builtin_amdgcn_readfirstlane(t.nrows);
+        nt = __builtin_amdgcn_readfirstlane(t.pad);
+    };
+    decode(logical, 0);
 
     // ---- global -> LDS direct loads --------------------------------------
     // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS at M0 + 16 l,
@@ -598,7 +612,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     const int lg_next = logical + nj;
     const bool more = lg_next < t_hi;
     if (more) {
-        decode(lg_next);
+        decode(lg_next, tile_i + 1);
         set_bases();
         lds_reads_done_barrier();
         prologue(s_w_next);
@@ -610,6 +624,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     s_w = s_w_next;
     s_w_next = t;
     logical = lg_next;
+    ++tile_i;
     }
 
 }
@@ -621,14 +636,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_l1(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
     __shared__ __attribute__((aligned(16))) uint8_t st2[kStageBytes];
     __shared__ float s_w[2][kBM];
-    gemm_persistent<kL1>(args, st0, st1, st2, s_w[0], s_w[1]);
+    __shared__ MTile s_tiles[kTileCache];
+    gemm_persistent<kL1>(args, st0, st1, st2, s_w[0], s_w[1], s_tiles);
 }
 
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_l2(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) uint8_t st0[kStageBytes];
     __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
     __shared__ __attribute__((aligned(16))) uint8_t st2[kStageBytes];
-    gemm_persistent<kL2>(args, st0, st1, st2, nullptr, nullptr);
+    __shared__ MTile s_tiles[kTileCache];
+    gemm_persistent<kL2>(args, st0, st1, st2, nullptr, nullptr, s_tiles);
 }
 
 }  // namespace moe
