@@ -86,8 +86,9 @@ int device_ok() {
 }
 
 // Workgroups of a persistent GEMM launch: one per CU (at most one fits, by
-// LDS), a multiple of 8 so that every XCD gets the same number, and no more
-// than there can be tiles.
+// LDS), a multiple of 8 so that every XCD gets the same number, no more than
+// there can be tiles, and enough that no workgroup gets more than kTileCache
+// tiles (workgroups beyond the CU count then wait for a free CU).
 unsigned gemm_grid(int64_t max_tiles) {
     static int cus[64];
     int dev = 0;
@@ -101,6 +102,9 @@ unsigned gemm_grid(int64_t max_tiles) {
     int64_t w = n / 8 * 8;
     const int64_t need = (max_tiles + 7) / 8 * 8;
     if (need < w) w = need;
+    const int64_t per_xcd = (max_tiles + 7) / 8;
+    const int64_t min_w = 8 * ((per_xcd + kTileCache - 1) / kTileCache);
+    if (w < min_w) w = min_w;
     return (unsigned)(w < 8 ? 8 : w);
 }
 

@@ -14,15 +14,15 @@
 // MI355X design (not the pages' SM100 one):
 //  - v_mfma_scale_f32_32x32x64_f8f6f4 with A = e4m3 (format 0), B = e2m1
 //    (format 4), scales per lane; fp32 accumulators in AGPRs.
-//  - 256 x 256 tile per 4-wave workgroup, each wave 128 x 128 (4 x 4 MFMA
-//    tiles); K steps of 128 staged through three LDS stages by direct
-//    global->LDS loads issued two steps ahead; 16-byte chunks XOR-swizzled so
+//  - 256 x 256 tile per 4-wave workgroup, each wave 64 rows x 256 columns
+//    (2 x 8 MFMA tiles); K steps of 128 staged through three LDS stages by
+//    direct global->LDS loads issued two steps ahead; 16-byte chunks XOR-swizzled so
 //    that the 16 lanes of each ds_read_b128 phase hit distinct banks of the
 //    64-bank LDS (A rows of 128 B: chunk ^ (row/2)%8; B rows of 64 B:
 //    chunk ^ (row/4)%4).
 //  - Expert-major m-tile table built on the device by the routing scan: no
-//    host synchronisation; surplus workgroups exit at once.
-//  - Workgroup ids are remapped so that each XCD (own L2) works on a
+//    host synchronisation.
+//  - Persistent workgroups, one per CU; each XCD (own L2) works through a
 //    contiguous run of tiles that share weights and activations.
 //  - L1 tiles hold 128 gate and the matching 128 up columns, split so that
 //    each wave has gate column j and up column j in the same lane and
@@ -46,7 +46,6 @@ namespace {
 
 constexpr int kL1 = 0;
 constexpr int kL2 = 1;
-constexpr int kTileCache = 256;  // tile records kept in LDS per workgroup
 constexpr int kGroupM = 4;  // m-tiles per tile-order group
 
 // Which expert-matrix row (output column) holds LDS B row `nrow` of tile nt.
@@ -112,7 +111,7 @@ __device__ __forceinline__ void dma_x1(uint32_t lds, const void* sbase, uint32_t
                  :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(sbase))
                  : "memory");
 }
-// Wait for this wave's direct loads except the newest 14 or 21 (or all), then a
+// Wait for this wave's direct loads except the newest 14, 21 or 22 (or all), then a
 // workgroup barrier.  No memory fence: the data already sits in LDS.
 __device__ __forceinline__ void barrier_after_vmcnt14() {
     asm volatile("s_waitcnt vmcnt(14) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -120,12 +119,20 @@ __device__ __forceinline__ void barrier_after_vmcnt14() {
 __device__ __forceinline__ void barrier_after_vmcnt21() {
     asm volatile("s_waitcnt vmcnt(21) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+__device__ __forceinline__ void barrier_after_vmcnt22() {
+    asm volatile("s_waitcnt vmcnt(22) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 __device__ __forceinline__ void barrier_after_vmcnt0() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 // Every wave's LDS reads are done (the stages may be overwritten).
 __device__ __forceinline__ void lds_reads_done_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// All of this wave's direct loads have landed (none may still write LDS when
+// the workgroup ends).
+__device__ __forceinline__ void wait_all_loads() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 // A copy of v that the compiler cannot compute before this point: keeps the
 // epilogue's per-lane address arithmetic (the same for every tile) from being
@@ -144,9 +151,11 @@ __device__ __forceinline__ int late_copy(int v) {
 // of 8 and the hardware places workgroup b on XCD b % 8; XCD x owns the
 // logical tiles [total*x/8, total*(x+1)/8) and its workgroups take them
 // round-robin, so the ~32 workgroups of an XCD work on consecutive tiles of
-// one group and share both operands through that XCD's L2.  After a tile's K
-// loop the first loads of the next tile go out before the epilogue, so their
-// latency (and the launch of a new workgroup) hide behind it.
+// one group and share both operands through that XCD's L2.  The stream of K
+// steps runs on across tiles: the last three steps of a tile issue the first
+// loads of the next one at the steady rate, so they land while the epilogue
+// runs.  (The host sizes the grid so that no workgroup has more than
+// kTileCache tiles.)
 template <int MODE>
 __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0, uint8_t* st1,
                                                 uint8_t* st2, float* s_wa, float* s_wb,
@@ -185,14 +194,13 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
         __syncthreads();
     }
     int e = 0, row0 = 0, nrows = 0, nt = 0, tile_i = 0;
-    auto decode = [&](int lg, int i) __attribute__((always_inline)) {
-        const MTile t = i < kTileCache ? s_tiles[i] : record(lg);
+    auto take = [&](const MTile& t) __attribute__((always_inline)) {
         e = __builtin_amdgcn_readfirstlane(t.expert);
         row0 = __builtin_amdgcn_readfirstlane(t.row0);
         nrows = __builtin_amdgcn_readfirstlane(t.nrows);
         nt = __builtin_amdgcn_readfirstlane(t.pad);
     };
-    decode(logical, 0);
+    take(s_tiles[0]);
 
     // ---- global -> LDS direct loads --------------------------------------
     // global_load_lds_dwordx4 writes lane l's 16 bytes to LDS at M0 + 16 l,
@@ -242,7 +250,11 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
         sb_base = g.SB + (int64_t)e * (Kdim / 128) * sb_step + (int64_t)b_r0 * 4;
     };
     set_bases();
-    const uint32_t lds_st0 = lds_addr(st0), lds_st1 = lds_addr(st1), lds_st2 = lds_addr(st2);
+    // LDS stages of the current step k, of k+1 and of k+2; the rotation runs
+    // on across tiles.
+    const uint8_t* cur = st0;
+    const uint8_t* next = st1;
+    const uint8_t* third = st2;
     const uint32_t w_dst16 = (uint32_t)(64 * wid * 16);
     const uint32_t w_dst4 = (uint32_t)(64 * wid * 4);
 
@@ -488,24 +500,29 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     // barrier: step k+1's stage is complete and step k's stage is free (all
     // its reads are done), so the first half of step k+3's loads goes into it
     // beside the MFMAs of Y, while X is read from step k+1's stage.  Loads go
-    // out one per two MFMAs, so the load path never backs up the MFMA issue.
-    // Every MFMA is fenced together with the reads/loads issued beside it, so
-    // the compiler keeps this order; the loop body is branch-free, and the
-    // last three steps run in a second loop that issues no new steps.
+    // out one per two MFMAs, so the load path never backs up the MFMA issue
+    // and LDS writes are spread evenly over the step.  Every MFMA is fenced
+    // together with the reads/loads issued beside it, so the compiler keeps
+    // this order; the loop body is branch-free.  (A wave issues at most one
+    // instruction per 4 cycles, so each 64-cycle MFMA leaves room for about
+    // 15 others: the loop keeps every window under that.)
     // First loads of a tile: its routing weights (L1), steps 0 and 1 and the
     // first half of step 2 -- 35 loads per wave (36 with the weights).  The
     // wait leaves the newest 21 in flight: the weights and step 0 have landed
     // (loads complete in order; stores issued in between only make the wait
     // longer).
-    auto prologue = [&](float* sw) __attribute__((always_inline)) {
+    auto issue_weights = [&](float* sw) __attribute__((always_inline)) {
         if (MODE == kL1) dma_x1(lds_addr(sw) + w_dst4, g.pool_w + row0, (uint32_t)(tid * 4));
-        issue_half(lds_st0, 0, 0);
-        issue_half(lds_st0, 0, 1);
+    };
+    auto prologue = [&](float* sw) __attribute__((always_inline)) {
+        issue_weights(sw);
+        issue_half(lds_addr(cur), 0, 0);
+        issue_half(lds_addr(cur), 0, 1);
         if (nk > 1) {
-            issue_half(lds_st1, 1, 0);
-            issue_half(lds_st1, 1, 1);
+            issue_half(lds_addr(next), 1, 0);
+            issue_half(lds_addr(next), 1, 1);
         }
-        if (nk > 2) issue_half(lds_st2, 2, 0);
+        if (nk > 2) issue_half(lds_addr(third), 2, 0);
     };
     auto wait_prologue = [&]() __attribute__((always_inline)) {
         if (nk > 2)
@@ -519,85 +536,129 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     float* s_w_next = s_wb;
     prologue(s_w);
     wait_prologue();
+    // Two instantiations of the tile loop: SEAM (nk >= 3) runs the K-step
+    // stream on across tiles; otherwise the next tile's prologue goes out
+    // after the K loop.  (One loop with both tails inside makes the register
+    // allocator spill the operand fragments.)
+    auto tile_loop = [&](auto seam) __attribute__((always_inline)) {
+    constexpr bool SEAM = decltype(seam)::value;
     for (;;) {
+    const int lg_next = logical + nj;
+    const bool more = lg_next < t_hi;
+    auto rotate = [&]() __attribute__((always_inline)) {
+        const uint8_t* t = cur;
+        cur = next;
+        next = third;
+        third = t;
+    };
     // The K loop, for a wave with ACT row tiles holding rows; every variant
     // issues the same loads and meets the same barriers.
     auto k_loop = [&](auto act) __attribute__((always_inline)) {
         SubFrags X, Y;
         ScaleWords Wc, Wn;  // words in use (shifted), words of the next step as read
-        read_all(X, Wn, st0, 0, act);
-        const uint8_t* cur = st0;
-        const uint8_t* next = st1;
-        const uint8_t* third = st2;
-        int k = 0;
-        for (; k + 3 < nk; ++k) {
-            const uint32_t dst2 = lds_addr(third);
+        read_all(X, Wn, cur, 0, act);
+        if constexpr (SEAM) {
+            // Steps k+2 and k+3 past the end of the tile are the next tile's
+            // steps 0, 1, 2.  The steady loop runs while both are this
+            // tile's; the last three steps run in a second loop whose scalar
+            // bases switch to the next tile (by selects: no branch in the
+            // body) once step nk-3 has sent its last load of this tile, beside
+            // MFMA 14 of its first half.  The last tile of a workgroup loads
+            // its own first steps again instead (harmless; waited for before
+            // the workgroup ends).  The barrier of step nk-1 waits for the next
+            // tile's step 0, which its second half reads (unused).
+            int k = 0;
+            for (; k + 3 < nk; ++k) {
+                const uint32_t dst2 = lds_addr(third);
     #pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                shift_for(Wc, Wn, g, act);
-                mfma_one(X, Wc, sub0, g, act);
-                read_piece(Y, cur, 1, g, act);
-                issue_spread(dst2, k + 2, 1, g);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            barrier_after_vmcnt14();
-            __builtin_amdgcn_sched_barrier(0);
-            const uint32_t dst3 = lds_addr(cur);
-    #pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                mfma_one(Y, Wc, sub1, g, act);
-                read_piece_and_scales(X, Wn, next, g, act);
-                issue_spread(dst3, k + 3, 0, g);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            const uint8_t* t = cur;
-            cur = next;
-            next = third;
-            third = t;
-        }
-        // The last min(nk, 3) steps issue no new steps.  Each is straight-line
-        // code (a branch inside would let the compiler sink MFMAs past the
-        // barrier); the first of them (when nk >= 3) sends the second half of the
-        // last step's loads, and its barrier then waits for step k+1 only.
-        auto tail_step = [&](auto issue_tag) __attribute__((always_inline)) {
-            constexpr bool kIssue = decltype(issue_tag)::value;
-            if (kIssue) issue_half(lds_addr(third), k + 2, 1);
-            __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                shift_for(Wc, Wn, g, act);
-                mfma_one(X, Wc, sub0, g, act);
-                read_piece(Y, cur, 1, g, act);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (kIssue)
+                for (int g = 0; g < 16; ++g) {
+                    shift_for(Wc, Wn, g, act);
+                    mfma_one(X, Wc, sub0, g, act);
+                    read_piece(Y, cur, 1, g, act);
+                    issue_spread(dst2, k + 2, 1, g);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 barrier_after_vmcnt14();
-            else
-                barrier_after_vmcnt0();
-            __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                mfma_one(Y, Wc, sub1, g, act);
-                read_piece_and_scales(X, Wn, next, g, act);  // on the last step: a stale stage, unused
                 __builtin_amdgcn_sched_barrier(0);
+                const uint32_t dst3 = lds_addr(cur);
+    #pragma unroll
+                for (int g = 0; g < 16; ++g) {
+                    mfma_one(Y, Wc, sub1, g, act);
+                    read_piece_and_scales(X, Wn, next, g, act);
+                    issue_spread(dst3, k + 3, 0, g);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                rotate();
             }
-            const uint8_t* t = cur;
-            cur = next;
-            next = third;
-            third = t;
-            ++k;
-        };
-        if (nk >= 3) tail_step(std::true_type{});
-        while (k < nk) tail_step(std::false_type{});
+            const MTile nrec = s_tiles[more ? tile_i + 1 : tile_i];
+            const int n_e = __builtin_amdgcn_readfirstlane(nrec.expert);
+            const int n_row0 = __builtin_amdgcn_readfirstlane(nrec.row0);
+            const int n_nrows = __builtin_amdgcn_readfirstlane(nrec.nrows);
+            const int n_nt = __builtin_amdgcn_readfirstlane(nrec.pad);
+            for (; k < nk; ++k) {
+                const int s2 = k + 2 < nk ? k + 2 : k + 2 - nk;
+                const uint32_t dst2 = lds_addr(third);
+    #pragma unroll
+                for (int g = 0; g < 16; ++g) {
+                    shift_for(Wc, Wn, g, act);
+                    mfma_one(X, Wc, sub0, g, act);
+                    if (g == 14) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        const bool sw = k == nk - 3;
+                        e = sw ? n_e : e;
+                        row0 = sw ? n_row0 : row0;
+                        nrows = sw ? n_nrows : nrows;
+                        nt = sw ? n_nt : nt;
+                        set_bases();
+                    }
+                    read_piece(Y, cur, 1, g, act);
+                    issue_spread(dst2, s2, 1, g);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                barrier_after_vmcnt14();
+                __builtin_amdgcn_sched_barrier(0);
+                const uint32_t dst3 = lds_addr(cur);
+    #pragma unroll
+                for (int g = 0; g < 16; ++g) {
+                    mfma_one(Y, Wc, sub1, g, act);
+                    read_piece_and_scales(X, Wn, next, g, act);
+                    issue_spread(dst3, k + 3 - nk, 0, g);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                rotate();
+            }
+        } else {
+            // nk < 3: no step issues loads; the next tile's prologue goes out
+            // after the K loop.
+            for (int k = 0; k < nk; ++k) {
+    #pragma unroll
+                for (int g = 0; g < 16; ++g) {
+                    shift_for(Wc, Wn, g, act);
+                    mfma_one(X, Wc, sub0, g, act);
+                    read_piece(Y, cur, 1, g, act);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                barrier_after_vmcnt0();
+                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int g = 0; g < 16; ++g) {
+                    mfma_one(Y, Wc, sub1, g, act);
+                    read_piece_and_scales(X, Wn, next, g, act);  // on the last step: a stale stage, unused
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                rotate();
+            }
+        }
     };
-    // (L2 only: a short L1 tile is bound by its loads, and the variants cost
-    // the L1 kernel registers)
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const int c_row0 = row0, c_nrows = nrows, c_nt = nt;
+    // (L2 only: a short L1 tile is bound by its loads, and the variants cost
+    // the L1 kernel registers)
     const int nact = MODE == kL1 ? 2 : (nrows > 64 * wm + 32 ? 2 : (nrows > 64 * wm ? 1 : 0));
     if (nact == 2)
         k_loop(std::integral_constant<int, 2>{});
@@ -606,27 +667,37 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     else
         k_loop(std::integral_constant<int, 0>{});
 
-    // next tile: once every wave is done reading the stages, its first loads
-    // go out, then this tile's epilogue runs while they fly
-    const int c_row0 = row0, c_nrows = nrows, c_nt = nt;
-    const int lg_next = logical + nj;
-    const bool more = lg_next < t_hi;
-    if (more) {
-        decode(lg_next, tile_i + 1);
+    if (SEAM) {
+        // the next tile's routing weights (L1); its step 0 is waited for
+        // after the epilogue, leaving its step 1, the first half of step 2
+        // and the weights in flight
+        issue_weights(s_w_next);
+    } else if (more) {
+        // once every wave is done reading the stages, the next tile's first
+        // loads go out, then this tile's epilogue runs while they fly
+        take(s_tiles[tile_i + 1]);
         set_bases();
         lds_reads_done_barrier();
         prologue(s_w_next);
     }
     epilogue(c_row0, c_nrows, c_nt, s_w);
     if (!more) break;
-    wait_prologue();
+    if (SEAM && MODE == kL1)
+        barrier_after_vmcnt22();
+    else
+        wait_prologue();
     float* t = s_w;
     s_w = s_w_next;
     s_w_next = t;
     logical = lg_next;
     ++tile_i;
     }
-
+    };
+    if (nk >= 3)
+        tile_loop(std::true_type{});
+    else
+        tile_loop(std::false_type{});
+    wait_all_loads();
 }
 
 }  // namespace

@@ -30,6 +30,10 @@ struct MTile {
     int32_t expert, row0, nrows, pad;
 };
 
+// Tile records a persistent GEMM workgroup keeps in LDS: the launch must give
+// no workgroup more tiles than this (at most ceil(ceil(tiles / 8) / (grid / 8))).
+constexpr int kTileCache = 256;
+
 // Block scales in "packed k-major" layout: one 4-byte word holds the UE8M0
 // bytes of the 4 consecutive 32-wide k-blocks of one 128-wide K step w, in
 // byte order (4w, 4w+2, 4w+1, 4w+3), and the words of one K step are stored
