@@ -134,6 +134,15 @@ __device__ __forceinline__ void lds_reads_done_barrier() {
 __device__ __forceinline__ void wait_all_loads() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
+// Buffer resource over [base, base + bytes): raw buffer stores at offsets at or
+// past `bytes` are dropped by the hardware range check (third descriptor word
+// of a raw untyped gfx9 buffer).  The epilogues use it to skip the rows past
+// the end of a short tile without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // A copy of v that the compiler cannot compute before this point: keeps the
 // epilogue's per-lane address arithmetic (the same for every tile) from being
 // hoisted out of the tile loop, where it would hold registers across the K
@@ -386,11 +395,13 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     // thanks to the column order of the B rows each lane holds adjacent output
     // columns of that row, so rows go straight to global memory: 32 lanes
     // store one contiguous run of the row (no LDS, no lane exchanges).
-    // Full tiles (the common case) store without row checks, so the
-    // epilogue is straight-line code; partial tiles check each row.
+    // Stores go through buffer resources that end at the tile's last row, so
+    // rows past the end of a short tile are dropped without branches; a row
+    // tile with no rows at all is skipped (a wave-uniform test).
     if (MODE == kL2) {
         const int N = g.N;
         uint8_t* out_base = reinterpret_cast<uint8_t*>(g.out + (int64_t)row0 * N + nt * kBN);  // wave-uniform
+        const __amdgpu_buffer_rsrc_t out_rs = rows_rsrc(out_base, nrows * N * 2);
         auto rows = [&](auto partial) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -401,14 +412,10 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                     float c[8];  // read from the accumulator registers where used
 #pragma unroll
                     for (int j = 0; j < 8; ++j) asm("v_accvgpr_read_b32 %0, %1" : "=v"(c[j]) : "a"(acc[i][j][r]));
-                    uint4 v;
-                    v.x = pack_bf16x2(c[0], c[1]);
-                    v.y = pack_bf16x2(c[2], c[3]);
-                    v.z = pack_bf16x2(c[4], c[5]);
-                    v.w = pack_bf16x2(c[6], c[7]);
+                    const u32x4 v = {pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]),
+                                     pack_bf16x2(c[4], c[5]), pack_bf16x2(c[6], c[7])};
                     const int lrow = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (!decltype(partial)::value || lrow < nrows)
-                        *reinterpret_cast<uint4*>(out_base + (uint32_t)(2 * (lrow * N + 8 * l32))) = v;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, out_rs, 2 * (lrow * N + 8 * l32), 0, 0);
                 }
             }
         };
@@ -426,6 +433,8 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
         const int I = g.I;
         uint8_t* q_base = g.act_q + (int64_t)row0 * I + nt * 128;                 // wave-uniform
         uint8_t* s_base = g.act_s + (int64_t)nt * g.sa_step + (int64_t)row0 * 4;  // wave-uniform
+        const __amdgpu_buffer_rsrc_t q_rs = rows_rsrc(q_base, nrows * I);
+        const __amdgpu_buffer_rsrc_t s_rs = rows_rsrc(s_base, nrows * 4);
         const int rsel = l32 & 7;
         const int G = l32 >> 3, gbyte = ((G & 1) << 1) | (G >> 1);
         auto rows = [&](auto fast, auto partial) __attribute__((always_inline)) {
@@ -477,11 +486,11 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                     const uint32_t bsel = rsel == 0 ? b[0] : rsel == 1 ? b[1] : rsel == 2 ? b[2] : b[3];
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
-                        if (!kPartial || lrow0 + rr < nrows)
-                            *reinterpret_cast<uint32_t*>(q_base + (uint32_t)((lrow0 + rr) * I + 4 * l32)) = codes[rr];
-                    // group G is byte (0, 2, 1, 3)[G] of the word
-                    if (rsel < 4 && (!kPartial || lrow0 + rsel < nrows))
-                        s_base[(uint32_t)((lrow0 + rsel) * 4 + gbyte)] = (uint8_t)bsel;
+                        __builtin_amdgcn_raw_buffer_store_b32(codes[rr], q_rs, (lrow0 + rr) * I + 4 * l32, 0, 0);
+                    // group G is byte (0, 2, 1, 3)[G] of the word; lanes with
+                    // rsel >= 4 store nothing (an offset past the range)
+                    const int s_off = rsel < 4 ? (lrow0 + rsel) * 4 + gbyte : 0x40000000;
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)bsel, s_rs, s_off, 0, 0);
                 }
             }
         };
