@@ -436,6 +436,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
         const __amdgpu_buffer_rsrc_t q_rs = rows_rsrc(q_base, nrows * I);
         const __amdgpu_buffer_rsrc_t s_rs = rows_rsrc(s_base, nrows * 4);
         const int rsel = l32 & 7;
+        const uint32_t bshift = 8u * (uint32_t)(rsel & 3);
         const int G = l32 >> 3, gbyte = ((G & 1) << 1) | (G >> 1);
         auto rows = [&](auto fast, auto partial) __attribute__((always_inline)) {
             constexpr bool kPartial = decltype(partial)::value;
@@ -447,34 +448,55 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                     const int lrow0 = 64 * wm + 32 * i + 8 * rq + 4 * h;
                     const float4 w4 = *reinterpret_cast<const float4*>(s_w + lrow0);
                     const float wr[4] = {w4.x, w4.y, w4.z, w4.w};
-                    float a[4][4];
+                    // In phases over the block's 16 elements (reads and bf16
+                    // rounding, exp, reciprocal, products), so that 16
+                    // independent chains hide the latency of the
+                    // transcendentals.
+                    float gt[4][4], up[4][4], a[4][4];
                     uint32_t m[4];
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
-                        const int r = 4 * rq + rr;
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj) {
-                            // gate and up rounded to bf16 by one conversion
-                            // read from the accumulator registers where used (else the
-                            // compiler copies all 256 up front and runs out of
-                            // registers for independent chains)
+                            // gate and up rounded to bf16 by one conversion,
+                            // read from the accumulator registers where used
+                            // (else the compiler copies all 256 up front)
+                            const int r = 4 * rq + rr;
                             float ga, ua;
                             asm("v_accvgpr_read_b32 %0, %1" : "=v"(ga) : "a"(acc[i][jj][r]));
                             asm("v_accvgpr_read_b32 %0, %1" : "=v"(ua) : "a"(acc[i][jj + 4][r]));
                             const uint32_t gu = pack_bf16x2(ga, ua);
-                            const float gt = bf16_lo(gu), up = bf16_hi(gu);
-                            float sl;
-                            if (decltype(fast)::value) {
-                                const float ex = __builtin_amdgcn_exp2f(-gt * 1.4426950408889634f);
-                                sl = gt * __builtin_amdgcn_rcpf(1.0f + ex);
-                            } else {
-                                sl = gt / (1.0f + expf(-gt));
-                            }
-                            a[rr][jj] = (sl * up) * wr[rr];
+                            gt[rr][jj] = bf16_lo(gu);
+                            up[rr][jj] = bf16_hi(gu);
                         }
+                    }
+                    if (decltype(fast)::value) {
+                        float ex[4][4];
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj)
+                                ex[rr][jj] = __builtin_amdgcn_exp2f(-gt[rr][jj] * 1.4426950408889634f);
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj) ex[rr][jj] = __builtin_amdgcn_rcpf(1.0f + ex[rr][jj]);
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj)
+                                a[rr][jj] = ((gt[rr][jj] * ex[rr][jj]) * up[rr][jj]) * wr[rr];
+                    } else {
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj)
+                                a[rr][jj] = ((gt[rr][jj] / (1.0f + expf(-gt[rr][jj]))) * up[rr][jj]) * wr[rr];
+                    }
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
                         m[rr] = __float_as_uint(fmaxf(fmaxf(fabsf(a[rr][0]), fabsf(a[rr][1])),
                                                       fmaxf(fabsf(a[rr][2]), fabsf(a[rr][3]))));
-                    }
                     group8_max_u32x4(m);
                     uint32_t codes[4], b[4];
 #pragma unroll
@@ -483,7 +505,10 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                         codes[rr] = pack_fp8x4(unscale(a[rr][0], b[rr]), unscale(a[rr][1], b[rr]),
                                                unscale(a[rr][2], b[rr]), unscale(a[rr][3], b[rr]));
                     }
-                    const uint32_t bsel = rsel == 0 ? b[0] : rsel == 1 ? b[1] : rsel == 2 ? b[2] : b[3];
+                    // the byte of row rsel (lanes rsel < 4 store it): one shift of
+                    // the four bytes packed in a word instead of a select chain
+                    const uint32_t b4 = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+                    const uint32_t bsel = b4 >> bshift;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
                         __builtin_amdgcn_raw_buffer_store_b32(codes[rr], q_rs, (lrow0 + rr) * I + 4 * l32, 0, 0);

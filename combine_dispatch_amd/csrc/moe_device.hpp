@@ -54,9 +54,12 @@ __device__ __forceinline__ uint32_t ue8m0_e4m3(float amax) {
     return (uint32_t)b;
 }
 
-// Same from the bits of a non-negative finite amax.
+// Same from the bits of a non-negative finite amax, in three integer ops:
+// adding 0x1FFFFF carries into the exponent field exactly when the
+// significand field exceeds 0x600000, and the 8 << 23 taken off first makes
+// the (arithmetic) shift give the exponent minus 8 directly.
 __device__ __forceinline__ uint32_t ue8m0_e4m3_bits(uint32_t bits) {
-    const int b = (int)(bits >> 23) - 8 + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    const int b = (int)(bits + 0x1FFFFFu - (8u << 23)) >> 23;
     return (uint32_t)(b < 0 ? 0 : (b > 254 ? 254 : b));
 }
 
