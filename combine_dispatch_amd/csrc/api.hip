@@ -72,6 +72,25 @@ Layout make_layout(const moe_shape_t* s) {
     return L;
 }
 
+// Packed weight scales (moe_pack_weight_scales): S1's words, then S2's.
+size_t packed_s1_bytes(const moe_shape_t* s) { return (size_t)s->E * 2 * s->I * (s->H / 32); }
+size_t packed_total_bytes(const moe_shape_t* s) {
+    return align_up(packed_s1_bytes(s)) + (size_t)s->E * s->H * (s->I / 32);
+}
+
+// Weight scales (ue8m0 [E][N][Kdim/32], rows of Kdim/128 words) -> the packed
+// k-major words the GEMMs load per K step, for both layers.
+void launch_pack_scales(const moe_shape_t* s, const uint8_t* S1, const uint8_t* S2, uint8_t* s1t,
+                        uint8_t* s2t, hipStream_t stream) {
+    const int H = s->H, I = s->I;
+    hipLaunchKernelGGL(k_scales_kmajor, dim3(2 * I / 64, s->E, (H / 128 + 63) / 64), dim3(256), 0,
+                       stream, reinterpret_cast<const uint32_t*>(S1), reinterpret_cast<uint32_t*>(s1t),
+                       2 * I, H / 128);
+    hipLaunchKernelGGL(k_scales_kmajor, dim3(H / 64, s->E, (I / 128 + 63) / 64), dim3(256), 0,
+                       stream, reinterpret_cast<const uint32_t*>(S2), reinterpret_cast<uint32_t*>(s2t),
+                       H, I / 128);
+}
+
 // gfx950 check, cached per device.
 int device_ok() {
     static int cache[64];  // 0 unknown, 1 ok, 2 bad
@@ -231,18 +250,30 @@ const char* moe_status_string(int status) {
     }
 }
 
-int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
-                      const int64_t* topk_idx, const float* topk_w, const uint8_t* W1q,
-                      const uint8_t* S1, const uint8_t* W2q, const uint8_t* S2, void* y,
-                      void* workspace, size_t workspace_bytes, moe_stream_t stream_) {
+}  // extern "C"
+
+namespace {
+
+// The layer.  With `packed` set, the weight scales come from a buffer filled
+// by moe_pack_weight_scales (S1, S2 unused); otherwise they are laid out
+// into the workspace first.
+int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
+                  const int64_t* topk_idx, const float* topk_w, const uint8_t* W1q,
+                  const uint8_t* S1, const uint8_t* W2q, const uint8_t* S2, const uint8_t* packed,
+                  void* y, void* workspace, size_t workspace_bytes, moe_stream_t stream_) {
     if (!shape_basic_ok(s)) return MOE_ERR_INVALID_ARG;
     const moe_options_t o = opt ? *opt : moe_default_options();
     if (!isnan(o.activation_clamp)) return MOE_ERR_UNSUPPORTED;
     if (s->H % kBN || s->I % 128) return MOE_ERR_UNSUPPORTED;
     if (s->T == 0) return MOE_OK;
-    if (!x || !topk_idx || !topk_w || !W1q || !S1 || !W2q || !S2 || !y) return MOE_ERR_INVALID_ARG;
-    if ((reinterpret_cast<uintptr_t>(S1) | reinterpret_cast<uintptr_t>(S2)) % 4)
-        return MOE_ERR_INVALID_ARG;  // scale rows are read as 4-byte words
+    if (!x || !topk_idx || !topk_w || !W1q || !W2q || !y) return MOE_ERR_INVALID_ARG;
+    if (packed) {
+        if (reinterpret_cast<uintptr_t>(packed) % kAlign) return MOE_ERR_INVALID_ARG;
+    } else {
+        if (!S1 || !S2) return MOE_ERR_INVALID_ARG;
+        if ((reinterpret_cast<uintptr_t>(S1) | reinterpret_cast<uintptr_t>(S2)) % 4)
+            return MOE_ERR_INVALID_ARG;  // scale rows are read as 4-byte words
+    }
     const Layout L = make_layout(s);
     if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
         return MOE_ERR_WORKSPACE;
@@ -260,17 +291,13 @@ int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void
     uint8_t* act_q = ws + L.act_q;
     uint8_t* act_s = ws + L.act_s;
     uint16_t* l2_out = reinterpret_cast<uint16_t*>(ws + L.l2_out);
-    uint8_t* s1t = ws + L.s1t;
-    uint8_t* s2t = ws + L.s2t;
+    const uint8_t* s1t = packed ? packed : ws + L.s1t;
+    const uint8_t* s2t = packed ? packed + align_up(packed_s1_bytes(s)) : ws + L.s2t;
 
     const int pc = prof_begin(stream);
     // weight scales into the packed k-major words the GEMMs load per K step
-    hipLaunchKernelGGL(k_scales_kmajor, dim3(2 * I / 64, s->E, (H / 128 + 63) / 64), dim3(256), 0,
-                       stream, reinterpret_cast<const uint32_t*>(S1), reinterpret_cast<uint32_t*>(s1t),
-                       2 * I, H / 128);
-    hipLaunchKernelGGL(k_scales_kmajor, dim3(H / 64, s->E, (I / 128 + 63) / 64), dim3(256), 0,
-                       stream, reinterpret_cast<const uint32_t*>(S2), reinterpret_cast<uint32_t*>(s2t),
-                       H, I / 128);
+    // (unless the caller packed them once)
+    if (!packed) launch_pack_scales(s, S1, S2, ws + L.s1t, ws + L.s2t, stream);
     prof_mark(pc, MOE_STAGE_WEIGHT_SCALES, stream);
     int rc = run_routing(s, L, topk_idx, topk_w, ws, counts, offsets, pool_src, slot_to_pool,
                          pool_w, stream, pc);
@@ -324,6 +351,49 @@ int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void
                        static_cast<const float*>(nullptr), H, K, static_cast<uint16_t*>(y));
     prof_mark(pc, MOE_STAGE_COMBINE, stream);
     return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
+                      const int64_t* topk_idx, const float* topk_w, const uint8_t* W1q,
+                      const uint8_t* S1, const uint8_t* W2q, const uint8_t* S2, void* y,
+                      void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+    return fused_forward(s, opt, x, topk_idx, topk_w, W1q, S1, W2q, S2, nullptr, y, workspace,
+                         workspace_bytes, stream);
+}
+
+size_t moe_packed_scales_bytes(const moe_shape_t* s) {
+    if (!shape_basic_ok(s) || s->H % kBN || s->I % 128) return 0;
+    return packed_total_bytes(s);
+}
+
+int moe_pack_weight_scales(const moe_shape_t* s, const uint8_t* S1, const uint8_t* S2,
+                           void* packed, size_t packed_bytes, moe_stream_t stream_) {
+    if (!shape_basic_ok(s)) return MOE_ERR_INVALID_ARG;
+    if (s->H % kBN || s->I % 128) return MOE_ERR_UNSUPPORTED;
+    if (!S1 || !S2 || !packed) return MOE_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(S1) | reinterpret_cast<uintptr_t>(S2)) % 4 ||
+        reinterpret_cast<uintptr_t>(packed) % kAlign)
+        return MOE_ERR_INVALID_ARG;
+    if (packed_bytes < packed_total_bytes(s)) return MOE_ERR_WORKSPACE;
+    if (!device_ok()) return MOE_ERR_DEVICE;
+    uint8_t* p = static_cast<uint8_t*>(packed);
+    launch_pack_scales(s, S1, S2, p, p + align_up(packed_s1_bytes(s)),
+                       reinterpret_cast<hipStream_t>(stream_));
+    return launch_status();
+}
+
+int moe_fused_forward_packed(const moe_shape_t* s, const moe_options_t* opt, const void* x,
+                             const int64_t* topk_idx, const float* topk_w, const uint8_t* W1q,
+                             const uint8_t* W2q, const void* packed_scales, void* y,
+                             void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+    if (!packed_scales) return MOE_ERR_INVALID_ARG;
+    return fused_forward(s, opt, x, topk_idx, topk_w, W1q, nullptr, W2q, nullptr,
+                         static_cast<const uint8_t*>(packed_scales), y, workspace,
+                         workspace_bytes, stream);
 }
 
 int moe_dispatch(const moe_shape_t* s, const void* x, const int64_t* topk_idx, const float* topk_w,

@@ -115,6 +115,37 @@ int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt /* NULL = d
                       moe_stream_t stream);
 
 /*
+ * Weight scales laid out once for many forward calls.  The pages' fused entry
+ * takes its L1 and L2 weights already transformed into the kernel's own
+ * layout ([P1] "tests/test_mega_moe.py" snippet, the fused call); here the
+ * FP4 codes stay as given and only the scales are re-laid: for each expert and
+ * each 128-wide K step, one 4-byte word per weight row holding the UE8M0 bytes
+ * of the step's four 32-wide k-blocks in the order (0, 2, 1, 3), the words of
+ * one step contiguous over rows.  The packed buffer holds S1's words, then,
+ * from the next 256-byte boundary, S2's.  moe_fused_forward does the same
+ * relayout into its workspace on every call.
+ *
+ * moe_packed_scales_bytes: bytes of that buffer for shape *s (host only; 0 on
+ * a bad or unsupported shape).
+ * moe_pack_weight_scales: fills `packed` (device, 256-byte aligned, at least
+ * moe_packed_scales_bytes(s) bytes, owned by the caller) from S1 and S2 (as in
+ * moe_fused_forward, 4-byte aligned).  Asynchronous on `stream`.  Errors as
+ * moe_fused_forward; a short buffer gives MOE_ERR_WORKSPACE.
+ * moe_fused_forward_packed: moe_fused_forward with the scales read from a
+ * buffer that moe_pack_weight_scales filled for the same shape and weights;
+ * the result is bit-identical.  The buffer must stay unchanged while calls
+ * that read it are in flight.
+ */
+size_t moe_packed_scales_bytes(const moe_shape_t* s);
+int moe_pack_weight_scales(const moe_shape_t* s, const uint8_t* S1, const uint8_t* S2,
+                           void* packed, size_t packed_bytes, moe_stream_t stream);
+int moe_fused_forward_packed(const moe_shape_t* s, const moe_options_t* opt /* NULL = defaults */,
+                             const void* x, const int64_t* topk_idx, const float* topk_w,
+                             const uint8_t* W1q, const uint8_t* W2q, const void* packed_scales,
+                             void* y, void* workspace, size_t workspace_bytes,
+                             moe_stream_t stream);
+
+/*
  * Dispatch only: routing metadata plus the expert-major pool.  [P3] sections
  * 3.1-3.2 and appendix A.2; [P1] "dispatch.cuh" snippets (per-expert count,
  * prefix sum, slot allocation, row copy).

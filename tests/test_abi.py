@@ -99,3 +99,24 @@ def test_host_side_errors_need_no_device(moe):
     assert L.moe_combine(ctypes.byref(moe.MoeShape(0, 256, 32, 1, 2)), null, null, null, null,
                          null) == moe.MOE_OK
     assert L.moe_combine(ctypes.byref(s), null, null, null, null, null) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_packed_scale_entry_points_host_side(moe):
+    L = moe.lib()
+    null = ctypes.c_void_p(0)
+    H, I, E = 7168, 2048, 32
+    # S1's words, then S2's from the next 256-byte boundary: the same bytes as S1, S2
+    s1 = E * 2 * I * (H // 32)
+    assert moe.moe_packed_scales_bytes(H, I, E) == (s1 + 255) // 256 * 256 + E * H * (I // 32)
+    assert moe.moe_packed_scales_bytes(200, I, E) == 0
+    s = moe.MoeShape(16, 256, 128, 4, 2)
+    assert L.moe_pack_weight_scales(ctypes.byref(s), null, null, null, 0,
+                                    null) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weight_scales(ctypes.byref(moe.MoeShape(16, 200, 128, 4, 2)), null, null,
+                                    null, 0, null) == moe.MOE_ERR_UNSUPPORTED
+    # a missing packed buffer, null tensors -> invalid argument before any launch
+    assert L.moe_fused_forward_packed(ctypes.byref(s), None, *[null] * 7, null, 0,
+                                      null) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_fused_forward_packed(ctypes.byref(moe.MoeShape(0, 256, 128, 4, 2)), None,
+                                      *[null] * 5, ctypes.c_void_p(256), null, null, 0,
+                                      null) == moe.MOE_OK

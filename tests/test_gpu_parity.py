@@ -250,6 +250,47 @@ def test_errors_are_reported():
     assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("case", [SMALL[1], SMALL[6]], ids=["ragged", "e257"])
+def test_packed_weight_scales(case):
+    """moe_pack_weight_scales writes the documented layout (S1's words then,
+    from the next 256-byte boundary, S2's; per expert and 128-wide K step one
+    word per weight row with the k-blocks in byte order 0, 2, 1, 3), and the
+    packed forward equals the canonical one bit for bit."""
+    import combine_dispatch_amd as moe
+    inp = small_inputs(case)
+    T, H, I, E, K = (inp[k] for k in ("T", "H", "I", "E", "K"))
+    dev = to_dev(inp)
+    nbytes = moe.moe_packed_scales_bytes(H, I, E)
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    moe.moe_pack_weight_scales(dev["S1"], dev["S2"], packed, E=E, H=H, I=I)
+    raw = packed.cpu().numpy()
+
+    def unpack(words, N, kdim):
+        nw = kdim // 128
+        w = words.reshape(E, nw, N, 4)[:, :, :, [0, 2, 1, 3]]
+        return np.ascontiguousarray(w.transpose(0, 2, 1, 3).reshape(E, N, kdim // 32))
+
+    s1 = E * 2 * I * (H // 32)
+    off2 = (s1 + 255) // 256 * 256
+    np.testing.assert_array_equal(unpack(raw[:s1], 2 * I, H), inp["S1"])
+    np.testing.assert_array_equal(unpack(raw[off2:off2 + E * H * (I // 32)], H, I), inp["S2"])
+
+    y_ref, ws_ref = run_forward(inp, dev)
+    ws = torch.empty(moe.moe_workspace_bytes(T, H, I, E, K), dtype=torch.uint8, device=DEV)
+    y = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    moe.moe_fused_forward_packed(dev["x"], dev["topk_idx"], dev["topk_w"], dev["W1q"],
+                                 dev["W2q"], packed, y, ws, E=E, I=I)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_bits(y), y_ref)
+    R = int(view(ws_ref, inp, "offsets")[-1])
+    for name in ("act_q", "act_s", "l2_out"):
+        np.testing.assert_array_equal(view(ws, inp, name, R), view(ws_ref, inp, name, R))
+    short = torch.empty(nbytes - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_pack_weight_scales(dev["S1"], dev["S2"], short, E=E, H=H, I=I)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+
+
 def test_exact_math_option_also_within_tolerance():
     import combine_dispatch_amd as moe
     inp = small_inputs(SMALL[1])
