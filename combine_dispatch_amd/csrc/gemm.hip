@@ -64,6 +64,24 @@ __device__ __forceinline__ int b_row(int nt, int nrow, int I) {
     return nt * kBN + 8 * c + j;
 }
 
+// The same for a narrow tile (at most 64 rows): every wave covers rows 0-63
+// and multiplies two of the eight column tiles, chosen so that its outputs
+// still fill whole quantisation groups (L1) or adjacent columns (L2):
+//  L1: lane column c of tile j is activation column 32(j%4) + c (gate in
+//      tiles 0-3, up in 4-7); wave w takes tiles w and w+4, i.e. gate and up
+//      of quantisation group w, one column per lane.
+//  L2: lane column c of tile j is output column 64(j/2) + 2c + j%2; wave w
+//      takes tiles 2w and 2w+1, two adjacent output columns per lane.
+// Row 0 of either order is the tile's first row, so the scalar bases agree.
+template <int MODE>
+__device__ __forceinline__ int b_row_narrow(int nt, int nrow, int I) {
+    const int j = nrow >> 5, c = nrow & 31;
+    if (MODE == kL1) return (j < 4 ? 0 : I) + nt * 128 + 32 * (j & 3) + c;
+    return nt * kBN + 64 * (j >> 1) + 2 * c + (j & 1);
+}
+// Tiles with at most this many rows run narrow.
+constexpr int kNarrowRows = 64;
+
 // MFMA operands of one 64-wide K sub-step for one wave: A fragments of its 2
 // row tiles, B fragments of the 8 column tiles.
 struct SubFrags {
@@ -249,6 +267,16 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     const uint32_t sa_off = (uint32_t)(4 * ((tid & ~63) + 32 * (tid & 1) + ((tid & 63) >> 1)));
     const int64_t sb_step = (int64_t)g.N * 4;
     const uint32_t sb_off = (uint32_t)((b_row<MODE>(0, 32 * (tid & 7) + (tid >> 3), g.I) - b_row<MODE>(0, 0, g.I)) * 4);
+    // the same lane offsets for the column order of narrow tiles
+    const uint32_t nb_off = (uint32_t)((b_row_narrow<MODE>(0, (tid >> 2), g.I) - b_row_narrow<MODE>(0, 0, g.I)) * b_ld + 16 * b_chunk);
+    const uint32_t nb_off0 = nb_off,
+                   nb_off1 = nb_off + (b_row_narrow<MODE>(0, 64, g.I) - b_row_narrow<MODE>(0, 0, g.I)) * b_ld,
+                   nb_off2 = nb_off + (b_row_narrow<MODE>(0, 128, g.I) - b_row_narrow<MODE>(0, 0, g.I)) * b_ld,
+                   nb_off3 = nb_off + (b_row_narrow<MODE>(0, 192, g.I) - b_row_narrow<MODE>(0, 0, g.I)) * b_ld;
+    const uint32_t nsb_off = (uint32_t)((b_row_narrow<MODE>(0, 32 * (tid & 7) + (tid >> 3), g.I) - b_row_narrow<MODE>(0, 0, g.I)) * 4);
+    // column order of the tile whose loads go out when NAR below is 2: 1 for
+    // a narrow tile (wave-uniform)
+    int lnar = 0;
     // scalar bases of the current tile
     const uint8_t *a_base, *b_base, *sa_base, *sb_base;
     auto set_bases = [&]() __attribute__((always_inline)) {
@@ -270,29 +298,42 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     // 14 loads per wave per step (8 A, 4 B, 2 scale dwords), load number
     // 0..13.  A step's loads go out in two halves of 7, spread one per two
     // MFMAs: first half-loads h = 0, second h = 1.
-    auto issue_piece = [&](uint32_t st, int kk, int g) __attribute__((always_inline)) {
+    // NAR: 0 a full tile; 1 a narrow tile, whose A rows past 63 are not
+    // needed (a 4-byte stand-in load keeps the count of loads per step); 2
+    // the column order chosen by lnar, all A rows loaded.
+    auto issue_piece = [&](uint32_t st, int kk, int p, auto nar) __attribute__((always_inline)) {
+        constexpr int NAR = decltype(nar)::value;
         const int k0 = kk * kBK;
-        if (g < 8) {
-            const uint32_t off = g == 0 ? a_off0 : g == 1 ? a_off1 : g == 2 ? a_off2 : g == 3 ? a_off3
-                               : g == 4 ? a_off4 : g == 5 ? a_off5 : g == 6 ? a_off6 : a_off7;
-            dma_x4(st + w_dst16 + 4096 * g, a_base + k0, off);
-        } else if (g < 12) {
-            const uint32_t off = g == 8 ? b_off0 : g == 9 ? b_off1 : g == 10 ? b_off2 : b_off3;
-            dma_x4(st + kStageA + w_dst16 + 4096 * (g - 8), b_base + k0 / 2, off);
-        } else if (g == 12) {
+        if (p < 8) {
+            const uint32_t off = p == 0 ? a_off0 : p == 1 ? a_off1 : p == 2 ? a_off2 : p == 3 ? a_off3
+                               : p == 4 ? a_off4 : p == 5 ? a_off5 : p == 6 ? a_off6 : a_off7;
+            if (NAR == 1 && p >= 2)
+                dma_x1(st + w_dst16 + 4096 * p, a_base + k0, a_off0);
+            else
+                dma_x4(st + w_dst16 + 4096 * p, a_base + k0, off);
+        } else if (p < 12) {
+            const uint32_t fo = p == 8 ? b_off0 : p == 9 ? b_off1 : p == 10 ? b_off2 : b_off3;
+            const uint32_t no = p == 8 ? nb_off0 : p == 9 ? nb_off1 : p == 10 ? nb_off2 : nb_off3;
+            const uint32_t off = NAR == 0 ? fo : NAR == 1 ? no : (lnar ? no : fo);
+            dma_x4(st + kStageA + w_dst16 + 4096 * (p - 8), b_base + k0 / 2, off);
+        } else if (p == 12) {
             dma_x1(st + kStageA + kStageB + w_dst4, sa_base + kk * sa_step, sa_off);
-        } else if (g == 13) {
-            dma_x1(st + kStageA + kStageB + kStageSA + w_dst4, sb_base + kk * sb_step, sb_off);
+        } else if (p == 13) {
+            const uint32_t off = NAR == 0 ? sb_off : NAR == 1 ? nsb_off : (lnar ? nsb_off : sb_off);
+            dma_x1(st + kStageA + kStageB + kStageSA + w_dst4, sb_base + kk * sb_step, off);
         }
     };
     // Load of half `hf` that goes beside MFMA number g (0..15) of a sub-step.
-    auto issue_spread = [&](uint32_t st, int kk, int hf, int g) __attribute__((always_inline)) {
-        if ((g & 1) == 0 && g < 14) issue_piece(st, kk, 7 * hf + (g >> 1));
+    auto issue_spread = [&](uint32_t st, int kk, int hf, int g, auto nar) __attribute__((always_inline)) {
+        if ((g & 1) == 0 && g < 14) issue_piece(st, kk, 7 * hf + (g >> 1), nar);
     };
-    auto issue_half = [&](uint32_t st, int kk, int hf) __attribute__((always_inline)) {
+    auto issue_half = [&](uint32_t st, int kk, int hf, auto nar) __attribute__((always_inline)) {
 #pragma unroll
-        for (int g = 0; g < 7; ++g) issue_piece(st, kk, 7 * hf + g);
+        for (int p = 0; p < 7; ++p) issue_piece(st, kk, 7 * hf + p, nar);
     };
+    const std::integral_constant<int, 0> nar_full;
+    const std::integral_constant<int, 1> nar_narrow;
+    const std::integral_constant<int, 2> nar_sel;
 
     v16f acc[2][8];
 
@@ -385,6 +426,62 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     };
     const std::integral_constant<int, 0> sub0;
     const std::integral_constant<int, 1> sub1;
+
+    // ---- narrow tiles ------------------------------------------------------
+    // Wave wid's two column tiles (see b_row_narrow); its B fragments and B
+    // scale words sit in slots 0 and 1 of SubFrags::b and ScaleWords::b, its
+    // accumulators in acc[i][0] and acc[i][1].
+    const int jn0 = MODE == kL1 ? wid : 2 * wid;
+    const int jn1 = MODE == kL1 ? wid + 4 : 2 * wid + 1;
+    // Reads of sub-step s, in the order the MFMAs use them: row tile 0 (two
+    // 16-byte pieces), column tiles jn0 and jn1, row tile 1 (two pieces).
+    auto read_piece_n = [&](SubFrags& f, const uint8_t* base, int s, int p) __attribute__((always_inline)) {
+        const uint8_t* sA = base;
+        const uint8_t* sB = base + kStageA;
+        auto read_a = [&](int i, int part) __attribute__((always_inline)) {
+            const uint8_t* rowp = sA + (l32 + 32 * i) * kBK;
+            const uint4 v = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * s + 2 * part + h) ^ a_sw));
+            if (part == 0) {
+                f.a[i][0] = (int)v.x; f.a[i][1] = (int)v.y; f.a[i][2] = (int)v.z; f.a[i][3] = (int)v.w;
+            } else {
+                f.a[i][4] = (int)v.x; f.a[i][5] = (int)v.y; f.a[i][6] = (int)v.z; f.a[i][7] = (int)v.w;
+            }
+        };
+        if (p < 2) {
+            read_a(0, p);
+        } else if (p < 4) {
+            const uint8_t* rowp = sB + (32 * (p == 2 ? jn0 : jn1) + l32) * (kBK / 2);
+            const uint4 v = *reinterpret_cast<const uint4*>(rowp + 16 * ((2 * s + h) ^ b_sw));
+            f.b[p - 2] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+        } else {
+            read_a(1, p - 4);
+        }
+    };
+    // Scale words of a step: the two A words of rows 0-63 and the B words of
+    // column tiles jn0 and jn1 (LDS word 8c + j is column tile j, lane column c).
+    auto read_scales_n = [&](ScaleWords& w, const uint8_t* base) __attribute__((always_inline)) {
+        const uint8_t* sSA = base + kStageA + kStageB;
+        const uint8_t* sSB = sSA + kStageSA;
+        const uint2 v = *reinterpret_cast<const uint2*>(sSA + 8 * l32);
+        w.a[0] = (int)v.x;
+        w.a[1] = (int)v.y;
+        w.b[0] = *reinterpret_cast<const int*>(sSB + 4 * (8 * l32 + jn0));
+        w.b[1] = *reinterpret_cast<const int*>(sSB + 4 * (8 * l32 + jn1));
+    };
+    auto shift_n = [&](ScaleWords& c, const ScaleWords& n) __attribute__((always_inline)) {
+        c.a[0] = (int)((uint32_t)n.a[0] >> hs);
+        c.a[1] = (int)((uint32_t)n.a[1] >> hs);
+        c.b[0] = (int)((uint32_t)n.b[0] >> hs);
+        c.b[1] = (int)((uint32_t)n.b[1] >> hs);
+    };
+    // MFMA q (0..3) of sub-step S: row tile q/2, column slot q%2.
+    auto mfma_n = [&](const SubFrags& f, const ScaleWords& w, auto sub, int q) __attribute__((always_inline)) {
+        constexpr int S = decltype(sub)::value;
+        const int i = q >> 1, jj = q & 1;
+        const v8i b = v8i{f.b[jj][0], f.b[jj][1], f.b[jj][2], f.b[jj][3], 0, 0, 0, 0};
+        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], b, acc[i][jj], 0, 4, S,
+                                                                      w.a[i], S, w.b[jj]);
+    };
 
     // The epilogue of a finished tile (its row0, nrows, nt and routing weights).
     auto epilogue = [&](const int row0, const int nrows, const int nt, const float* s_w) __attribute__((always_inline)) {
@@ -526,6 +623,84 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     }
     };
 
+    // The epilogue of a finished narrow tile (NA row tiles hold rows): every
+    // wave holds rows 0-63 of its two column tiles, acc[i][0] and acc[i][1].
+    auto epilogue_n = [&](const int row0, const int nrows, const int nt, const float* s_w, auto na) __attribute__((always_inline)) {
+        constexpr int NA = decltype(na)::value;
+        const int lane = late_copy(tid & 63);
+        const int h = lane >> 5, l32 = lane & 31;
+        if (MODE == kL2) {
+            // output columns 64*wid + 2*l32 + {0, 1}: one bf16 pair per row
+            const int N = g.N;
+            uint8_t* out_base = reinterpret_cast<uint8_t*>(g.out + (int64_t)row0 * N + nt * kBN);  // wave-uniform
+            const __amdgpu_buffer_rsrc_t out_rs = rows_rsrc(out_base, nrows * N * 2);
+            const int col = 64 * wid + 2 * l32;
+#pragma unroll
+            for (int i = 0; i < NA; ++i) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float c0, c1;
+                    asm("v_accvgpr_read_b32 %0, %1" : "=v"(c0) : "a"(acc[i][0][r]));
+                    asm("v_accvgpr_read_b32 %0, %1" : "=v"(c1) : "a"(acc[i][1][r]));
+                    const int lrow = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                    __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(c0, c1), out_rs, 2 * (lrow * N + col), 0, 0);
+                }
+            }
+        } else {
+            // activation column 32*wid + l32 of the tile's 128: quantisation
+            // group wid spans the 32 lanes of a half-wave (one row each)
+            const int I = g.I;
+            uint8_t* q_base = g.act_q + (int64_t)row0 * I + nt * 128 + 32 * wid;      // wave-uniform
+            uint8_t* s_base = g.act_s + (int64_t)nt * g.sa_step + (int64_t)row0 * 4;  // wave-uniform
+            const __amdgpu_buffer_rsrc_t q_rs = rows_rsrc(q_base, nrows * I);
+            const __amdgpu_buffer_rsrc_t s_rs = rows_rsrc(s_base, nrows * 4);
+            const int gbyte = ((wid & 1) << 1) | (wid >> 1);  // group wid in the word's byte order
+            const uint32_t bshift = 8u * (uint32_t)(l32 & 3);
+#pragma unroll
+            for (int i = 0; i < NA; ++i) {
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int lrow0 = 32 * i + 8 * rq + 4 * h;
+                    const float4 w4 = *reinterpret_cast<const float4*>(s_w + lrow0);
+                    const float wr[4] = {w4.x, w4.y, w4.z, w4.w};
+                    float gt[4], up[4], a[4];
+                    uint32_t m[4];
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        float ga, ua;
+                        asm("v_accvgpr_read_b32 %0, %1" : "=v"(ga) : "a"(acc[i][0][4 * rq + rr]));
+                        asm("v_accvgpr_read_b32 %0, %1" : "=v"(ua) : "a"(acc[i][1][4 * rq + rr]));
+                        const uint32_t gu = pack_bf16x2(ga, ua);
+                        gt[rr] = bf16_lo(gu);
+                        up[rr] = bf16_hi(gu);
+                    }
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        if (g.fast_math) {
+                            const float ex = __builtin_amdgcn_exp2f(-gt[rr] * 1.4426950408889634f);
+                            a[rr] = ((gt[rr] * __builtin_amdgcn_rcpf(1.0f + ex)) * up[rr]) * wr[rr];
+                        } else {
+                            a[rr] = ((gt[rr] / (1.0f + expf(-gt[rr]))) * up[rr]) * wr[rr];
+                        }
+                        m[rr] = __float_as_uint(fabsf(a[rr]));
+                    }
+                    group32_max_u32x4(m);
+                    uint32_t b[4];
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        b[rr] = ue8m0_e4m3_bits(m[rr]);
+                        const uint32_t code = pack_fp8x2(unscale(a[rr], b[rr]), 0.f);
+                        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, q_rs, (lrow0 + rr) * I + l32, 0, 0);
+                    }
+                    // lanes l32 = 0..3 store the scale byte of rows lrow0 + l32
+                    const uint32_t b4 = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+                    const int s_off = l32 < 4 ? (lrow0 + l32) * 4 + gbyte : 0x40000000;
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(b4 >> bshift), s_rs, s_off, 0, 0);
+                }
+            }
+        }
+    };
+
     // ---- main loop: three LDS stages, sub-step pipelined operands ---------
     // X holds sub-step 0 and Y sub-step 1 of the current step k.  While the 16
     // MFMAs of X run, Y is read from step k's stage and the second half of
@@ -550,13 +725,13 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     };
     auto prologue = [&](float* sw) __attribute__((always_inline)) {
         issue_weights(sw);
-        issue_half(lds_addr(cur), 0, 0);
-        issue_half(lds_addr(cur), 0, 1);
+        issue_half(lds_addr(cur), 0, 0, nar_sel);
+        issue_half(lds_addr(cur), 0, 1, nar_sel);
         if (nk > 1) {
-            issue_half(lds_addr(next), 1, 0);
-            issue_half(lds_addr(next), 1, 1);
+            issue_half(lds_addr(next), 1, 0, nar_sel);
+            issue_half(lds_addr(next), 1, 1, nar_sel);
         }
-        if (nk > 2) issue_half(lds_addr(third), 2, 0);
+        if (nk > 2) issue_half(lds_addr(third), 2, 0, nar_sel);
     };
     auto wait_prologue = [&]() __attribute__((always_inline)) {
         if (nk > 2)
@@ -568,6 +743,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     };
     float* s_w = s_wa;
     float* s_w_next = s_wb;
+    lnar = nrows <= kNarrowRows ? 1 : 0;
     prologue(s_w);
     wait_prologue();
     // Two instantiations of the tile loop: SEAM (nk >= 3) runs the K-step
@@ -609,7 +785,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                     shift_for(Wc, Wn, g, act);
                     mfma_one(X, Wc, sub0, g, act);
                     read_piece(Y, cur, 1, g, act);
-                    issue_spread(dst2, k + 2, 1, g);
+                    issue_spread(dst2, k + 2, 1, g, nar_full);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 barrier_after_vmcnt14();
@@ -619,7 +795,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                 for (int g = 0; g < 16; ++g) {
                     mfma_one(Y, Wc, sub1, g, act);
                     read_piece_and_scales(X, Wn, next, g, act);
-                    issue_spread(dst3, k + 3, 0, g);
+                    issue_spread(dst3, k + 3, 0, g, nar_full);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 rotate();
@@ -629,6 +805,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
             const int n_row0 = __builtin_amdgcn_readfirstlane(nrec.row0);
             const int n_nrows = __builtin_amdgcn_readfirstlane(nrec.nrows);
             const int n_nt = __builtin_amdgcn_readfirstlane(nrec.pad);
+            lnar = 0;  // this tile is full
             for (; k < nk; ++k) {
                 const int s2 = k + 2 < nk ? k + 2 : k + 2 - nk;
                 const uint32_t dst2 = lds_addr(third);
@@ -643,10 +820,11 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                         row0 = sw ? n_row0 : row0;
                         nrows = sw ? n_nrows : nrows;
                         nt = sw ? n_nt : nt;
+                        lnar = sw ? (n_nrows <= kNarrowRows ? 1 : 0) : lnar;
                         set_bases();
                     }
                     read_piece(Y, cur, 1, g, act);
-                    issue_spread(dst2, s2, 1, g);
+                    issue_spread(dst2, s2, 1, g, nar_sel);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 barrier_after_vmcnt14();
@@ -656,7 +834,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                 for (int g = 0; g < 16; ++g) {
                     mfma_one(Y, Wc, sub1, g, act);
                     read_piece_and_scales(X, Wn, next, g, act);
-                    issue_spread(dst3, k + 3 - nk, 0, g);
+                    issue_spread(dst3, k + 3 - nk, 0, g, nar_sel);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 rotate();
@@ -684,6 +862,119 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
             }
         }
     };
+    // The K loop of a narrow tile with NA (1 or 2) row tiles holding rows:
+    // 2*NA MFMAs per sub-step, the same 14 loads per step and the same
+    // barriers as a full tile, so the two kinds of tile chain freely.  Read r
+    // of a sub-step goes beside MFMA r*NM/RP, load piece p of a half beside
+    // MFMA p*NM/7.
+    auto k_loop_n = [&](auto na) __attribute__((always_inline)) {
+        constexpr int NA = decltype(na)::value;
+        constexpr int NM = 2 * NA;
+        constexpr int RP = NA == 2 ? 6 : 4;
+        SubFrags X, Y;
+        ScaleWords Wc, Wn;
+        auto reads_beside = [&](SubFrags& f, const uint8_t* base, int s, int q) __attribute__((always_inline)) {
+#pragma unroll
+            for (int r = 0; r < RP; ++r)
+                if (r * NM / RP == q) read_piece_n(f, base, s, r);
+        };
+        auto loads_beside = [&](uint32_t st, int kk, int hf, int q, auto nar) __attribute__((always_inline)) {
+#pragma unroll
+            for (int p = 0; p < 7; ++p)
+                if (p * NM / 7 == q) issue_piece(st, kk, 7 * hf + p, nar);
+        };
+#pragma unroll
+        for (int r = 0; r < RP; ++r) read_piece_n(X, cur, 0, r);
+        read_scales_n(Wn, cur);
+        if constexpr (SEAM) {
+            // as in k_loop: a steady loop, then the last three steps, whose
+            // loads past the tile's end are the next tile's first steps
+            int k = 0;
+            for (; k + 3 < nk; ++k) {
+                const uint32_t dst2 = lds_addr(third);
+    #pragma unroll
+                for (int q = 0; q < NM; ++q) {
+                    if (q == 0) shift_n(Wc, Wn);
+                    mfma_n(X, Wc, sub0, q);
+                    reads_beside(Y, cur, 1, q);
+                    loads_beside(dst2, k + 2, 1, q, nar_narrow);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                barrier_after_vmcnt14();
+                __builtin_amdgcn_sched_barrier(0);
+                const uint32_t dst3 = lds_addr(cur);
+    #pragma unroll
+                for (int q = 0; q < NM; ++q) {
+                    mfma_n(Y, Wc, sub1, q);
+                    reads_beside(X, next, 0, q);
+                    if (q == 0) read_scales_n(Wn, next);
+                    loads_beside(dst3, k + 3, 0, q, nar_narrow);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                rotate();
+            }
+            const MTile nrec = s_tiles[more ? tile_i + 1 : tile_i];
+            const int n_e = __builtin_amdgcn_readfirstlane(nrec.expert);
+            const int n_row0 = __builtin_amdgcn_readfirstlane(nrec.row0);
+            const int n_nrows = __builtin_amdgcn_readfirstlane(nrec.nrows);
+            const int n_nt = __builtin_amdgcn_readfirstlane(nrec.pad);
+            lnar = 1;  // this tile is narrow
+            for (; k < nk; ++k) {
+                const int s2 = k + 2 < nk ? k + 2 : k + 2 - nk;
+                const uint32_t dst2 = lds_addr(third);
+    #pragma unroll
+                for (int q = 0; q < NM; ++q) {
+                    if (q == 0) shift_n(Wc, Wn);
+                    mfma_n(X, Wc, sub0, q);
+                    reads_beside(Y, cur, 1, q);
+                    loads_beside(dst2, s2, 1, q, nar_sel);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                {
+                    // this half's loads are out: switch to the next tile
+                    const bool sw = k == nk - 3;
+                    e = sw ? n_e : e;
+                    row0 = sw ? n_row0 : row0;
+                    nrows = sw ? n_nrows : nrows;
+                    nt = sw ? n_nt : nt;
+                    lnar = sw ? (n_nrows <= kNarrowRows ? 1 : 0) : lnar;
+                    set_bases();
+                }
+                barrier_after_vmcnt14();
+                __builtin_amdgcn_sched_barrier(0);
+                const uint32_t dst3 = lds_addr(cur);
+    #pragma unroll
+                for (int q = 0; q < NM; ++q) {
+                    mfma_n(Y, Wc, sub1, q);
+                    reads_beside(X, next, 0, q);
+                    if (q == 0) read_scales_n(Wn, next);
+                    loads_beside(dst3, k + 3 - nk, 0, q, nar_sel);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                rotate();
+            }
+        } else {
+            for (int k = 0; k < nk; ++k) {
+    #pragma unroll
+                for (int q = 0; q < NM; ++q) {
+                    if (q == 0) shift_n(Wc, Wn);
+                    mfma_n(X, Wc, sub0, q);
+                    reads_beside(Y, cur, 1, q);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                barrier_after_vmcnt0();
+                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int q = 0; q < NM; ++q) {
+                    mfma_n(Y, Wc, sub1, q);
+                    reads_beside(X, next, 0, q);  // on the last step: a stale stage, unused
+                    if (q == 0) read_scales_n(Wn, next);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                rotate();
+            }
+        }
+    };
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -691,15 +982,22 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     const int c_row0 = row0, c_nrows = nrows, c_nt = nt;
+    const bool c_narrow = nrows <= kNarrowRows;
     // (L2 only: a short L1 tile is bound by its loads, and the variants cost
     // the L1 kernel registers)
     const int nact = MODE == kL1 ? 2 : (nrows > 64 * wm + 32 ? 2 : (nrows > 64 * wm ? 1 : 0));
-    if (nact == 2)
+    if (c_narrow) {
+        if (nrows > 32)
+            k_loop_n(std::integral_constant<int, 2>{});
+        else
+            k_loop_n(std::integral_constant<int, 1>{});
+    } else if (nact == 2) {
         k_loop(std::integral_constant<int, 2>{});
-    else if (nact == 1)
+    } else if (nact == 1) {
         k_loop(std::integral_constant<int, 1>{});
-    else
+    } else {
         k_loop(std::integral_constant<int, 0>{});
+    }
 
     if (SEAM) {
         // the next tile's routing weights (L1); its step 0 is waited for
@@ -711,10 +1009,16 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
         // loads go out, then this tile's epilogue runs while they fly
         take(s_tiles[tile_i + 1]);
         set_bases();
+        lnar = nrows <= kNarrowRows ? 1 : 0;
         lds_reads_done_barrier();
         prologue(s_w_next);
     }
-    epilogue(c_row0, c_nrows, c_nt, s_w);
+    if (!c_narrow)
+        epilogue(c_row0, c_nrows, c_nt, s_w);
+    else if (c_nrows > 32)
+        epilogue_n(c_row0, c_nrows, c_nt, s_w, std::integral_constant<int, 2>{});
+    else
+        epilogue_n(c_row0, c_nrows, c_nt, s_w, std::integral_constant<int, 1>{});
     if (!more) break;
     if (SEAM && MODE == kL1)
         barrier_after_vmcnt22();

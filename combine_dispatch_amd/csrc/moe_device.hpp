@@ -109,6 +109,20 @@ __device__ __forceinline__ void group8_max_u32x4(uint32_t (&m)[4]) {
     for (int q = 0; q < 4; ++q) m[q] = max(m[q], dpp_u32<kDppQuadSwap2>(m[q]));
 }
 
+// Max over each aligned group of 32 lanes of four non-negative values held as
+// float bits: the 8-lane max, then lane i <-> 15-i inside each 16 (DPP row
+// mirror), then the two 16-lane halves of each 32 (ds_swizzle, xor 16).
+constexpr int kDppRowMirror = 0x140;
+constexpr int kSwizzleXor16 = 0x401F;  // bit-mask mode: and 0x1F, or 0, xor 0x10
+__device__ __forceinline__ void group32_max_u32x4(uint32_t (&m)[4]) {
+    group8_max_u32x4(m);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m[q] = max(m[q], dpp_u32<kDppRowMirror>(m[q]));
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        m[q] = max(m[q], (uint32_t)__builtin_amdgcn_ds_swizzle((int)m[q], kSwizzleXor16));
+}
+
 // Max over each aligned group of 8 lanes (all lanes get it): mirror inside
 // the 8, then the two quad swaps.
 __device__ __forceinline__ float group8_max(float v) {
