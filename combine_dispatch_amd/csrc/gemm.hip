@@ -160,6 +160,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(void* base, int byte
     return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
 }
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// Cache policy of the epilogue stores: non-temporal (the gfx940-family NT
+// bit).  The outputs are read back only by the next kernel, long after they
+// have left the caches, so they should not push out the operand tiles that
+// the XCD's workgroups share through its L2.
+constexpr int kStoreNT = 2;
 
 // A copy of v that the compiler cannot compute before this point: keeps the
 // epilogue's per-lane address arithmetic (the same for every tile) from being
@@ -512,7 +517,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                     const u32x4 v = {pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]),
                                      pack_bf16x2(c[4], c[5]), pack_bf16x2(c[6], c[7])};
                     const int lrow = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                    __builtin_amdgcn_raw_buffer_store_b128(v, out_rs, 2 * (lrow * N + 8 * l32), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(v, out_rs, 2 * (lrow * N + 8 * l32), 0, kStoreNT);
                 }
             }
         };
@@ -608,7 +613,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                     const uint32_t bsel = b4 >> bshift;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
-                        __builtin_amdgcn_raw_buffer_store_b32(codes[rr], q_rs, (lrow0 + rr) * I + 4 * l32, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(codes[rr], q_rs, (lrow0 + rr) * I + 4 * l32, 0, kStoreNT);
                     // group G is byte (0, 2, 1, 3)[G] of the word; lanes with
                     // rsel >= 4 store nothing (an offset past the range)
                     const int s_off = rsel < 4 ? (lrow0 + rsel) * 4 + gbyte : 0x40000000;
@@ -643,7 +648,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                     asm("v_accvgpr_read_b32 %0, %1" : "=v"(c0) : "a"(acc[i][0][r]));
                     asm("v_accvgpr_read_b32 %0, %1" : "=v"(c1) : "a"(acc[i][1][r]));
                     const int lrow = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                    __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(c0, c1), out_rs, 2 * (lrow * N + col), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(c0, c1), out_rs, 2 * (lrow * N + col), 0, kStoreNT);
                 }
             }
         } else {
@@ -690,7 +695,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                     for (int rr = 0; rr < 4; ++rr) {
                         b[rr] = ue8m0_e4m3_bits(m[rr]);
                         const uint32_t code = pack_fp8x2(unscale(a[rr], b[rr]), 0.f);
-                        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, q_rs, (lrow0 + rr) * I + l32, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, q_rs, (lrow0 + rr) * I + l32, 0, kStoreNT);
                     }
                     // lanes l32 = 0..3 store the scale byte of rows lrow0 + l32
                     const uint32_t b4 = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);

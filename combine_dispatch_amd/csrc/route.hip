@@ -388,7 +388,9 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
         out.y = pack_bf16x2(acc[2], acc[3]);
         out.z = pack_bf16x2(acc[4], acc[5]);
         out.w = pack_bf16x2(acc[6], acc[7]);
-        *reinterpret_cast<uint4*>(y + t * H + c0) = out;
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(u32x4{out.x, out.y, out.z, out.w},
+                                    reinterpret_cast<u32x4*>(y + t * H + c0));  // streamed out
     }
 }
 
