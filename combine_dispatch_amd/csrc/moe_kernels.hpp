@@ -8,7 +8,7 @@
 namespace moe {
 
 // Routing: one wave owns a segment of kSegSlots consecutive flat slots.
-constexpr int kSegSlots = 1024;
+constexpr int kSegSlots = 256;
 constexpr int kRouteWaves = 4;  // waves per routing block
 constexpr int kRouteThreads = kRouteWaves * 64;
 

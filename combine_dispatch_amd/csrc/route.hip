@@ -8,7 +8,7 @@
 // Differences from the pages' design, for one GPU and a deterministic result:
 //  - slots are ranked stably (ascending flat slot t*K+k inside an expert)
 //    instead of by atomic arrival order;
-//  - the histogram is privatised per wave in LDS over fixed 1024-slot
+//  - the histogram is privatised per wave in LDS over fixed kSegSlots-slot
 //    segments, so the ranking pass can start each segment from an exact base;
 //  - the token row is quantised to e4m3 while it is copied (the pages pull
 //    rows that are already FP8; quantising per row before or after the copy
@@ -18,7 +18,7 @@
 
 namespace moe {
 
-// a1: per-segment expert histogram.  One wave per 1024-slot segment, LDS
+// a1: per-segment expert histogram.  One wave per kSegSlots-slot segment, LDS
 // atomics on a per-wave histogram.  Indices >= E are counted as errors and
 // otherwise treated as masked.
 __global__ __launch_bounds__(kRouteThreads) void k_route_count(
