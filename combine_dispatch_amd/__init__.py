@@ -47,8 +47,8 @@ class MoeOptions(ctypes.Structure):
 
 class MoeWorkspaceViews(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
-                ("counts", "offsets", "pool_src", "slot_to_pool", "pool_w", "pool_q", "pool_s",
-                 "act_q", "act_s", "l2_out", "capacity_rows")]
+                ("counts", "offsets", "pool_src", "slot_to_pool", "pool_w", "pool_tok", "x_q",
+                 "x_s", "pool_s", "act_q", "act_s", "l2_out", "capacity_rows")]
 
 
 class MoeError(RuntimeError):

@@ -20,7 +20,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
     size_t seg_hist, seg_base, seg_err, counts, offsets, mtiles, num_mtiles, err_flag;
-    size_t pool_src, slot_to_pool, pool_w, pool_q, pool_s, act_q, act_s, l2_out, s1t, s2t, tok_s;
+    size_t pool_src, slot_to_pool, pool_w, pool_tok, x_q, pool_s, act_q, act_s, l2_out, s1t, s2t,
+        tok_s;
     size_t routing_end;  // bytes moe_dispatch needs
     size_t total;
     int64_t cap;         // pool rows incl. tile padding
@@ -60,7 +61,8 @@ Layout make_layout(const moe_shape_t* s) {
     L.pool_src = take(sizeof(int32_t) * L.cap);
     L.slot_to_pool = take(sizeof(int32_t) * (TK + 1));
     L.pool_w = take(sizeof(float) * L.cap);
-    L.pool_q = take((size_t)L.cap * s->H);
+    L.pool_tok = take(sizeof(int32_t) * L.cap);
+    L.x_q = take((size_t)s->T * s->H);
     L.pool_s = take((size_t)L.cap * (s->H / 32));
     L.act_q = take((size_t)L.cap * s->I);
     L.act_s = take((size_t)L.cap * (s->I / 32));
@@ -159,7 +161,7 @@ int bits_for(int E) {
 
 // a1-a3 into caller-visible arrays; the segment scratch lives at ws.
 int run_routing(const moe_shape_t* s, const Layout& L, const int64_t* topk_idx, const float* topk_w,
-                uint8_t* ws, int32_t* counts, int32_t* offsets, int32_t* pool_src,
+                uint8_t* ws, int32_t* pool_tok, int32_t* counts, int32_t* offsets, int32_t* pool_src,
                 int32_t* slot_to_pool, float* pool_w, hipStream_t stream, int pc = -1) {
     const int64_t TK = (int64_t)s->T * s->K;
     const int E = s->E;
@@ -179,7 +181,8 @@ int run_routing(const moe_shape_t* s, const Layout& L, const int64_t* topk_idx, 
                        reinterpret_cast<int32_t*>(ws + L.err_flag));
     prof_mark(pc, MOE_STAGE_ROUTE_SCAN, stream);
     hipLaunchKernelGGL(k_route_scatter, dim3(nblk), dim3(kRouteThreads), lds, stream, topk_idx,
-                       topk_w, TK, E, bits_for(E), seg_base, pool_src, slot_to_pool, pool_w);
+                       topk_w, TK, E, bits_for(E), s->K, seg_base, pool_src, slot_to_pool, pool_w,
+                       pool_tok);
     prof_mark(pc, MOE_STAGE_ROUTE_SCATTER, stream);
     return launch_status();
 }
@@ -229,7 +232,9 @@ int moe_workspace_views(const moe_shape_t* s, moe_workspace_views_t* v) {
     v->pool_src = (int64_t)L.pool_src;
     v->slot_to_pool = (int64_t)L.slot_to_pool;
     v->pool_w = (int64_t)L.pool_w;
-    v->pool_q = (int64_t)L.pool_q;
+    v->pool_tok = (int64_t)L.pool_tok;
+    v->x_q = (int64_t)L.x_q;
+    v->x_s = (int64_t)L.tok_s;
     v->pool_s = (int64_t)L.pool_s;
     v->act_q = (int64_t)L.act_q;
     v->act_s = (int64_t)L.act_s;
@@ -265,6 +270,7 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     const moe_options_t o = opt ? *opt : moe_default_options();
     if (!isnan(o.activation_clamp)) return MOE_ERR_UNSUPPORTED;
     if (s->H % kBN || s->I % 128) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)s->T * s->H >= (int64_t(1) << 32)) return MOE_ERR_UNSUPPORTED;  // 32-bit row offsets
     if (s->T == 0) return MOE_OK;
     if (!x || !topk_idx || !topk_w || !W1q || !W2q || !y) return MOE_ERR_INVALID_ARG;
     if (packed) {
@@ -286,7 +292,8 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     int32_t* pool_src = reinterpret_cast<int32_t*>(ws + L.pool_src);
     int32_t* slot_to_pool = reinterpret_cast<int32_t*>(ws + L.slot_to_pool);
     float* pool_w = reinterpret_cast<float*>(ws + L.pool_w);
-    uint8_t* pool_q = ws + L.pool_q;
+    int32_t* pool_tok = reinterpret_cast<int32_t*>(ws + L.pool_tok);
+    uint8_t* x_q = ws + L.x_q;
     uint8_t* pool_s = ws + L.pool_s;
     uint8_t* act_q = ws + L.act_q;
     uint8_t* act_s = ws + L.act_s;
@@ -299,27 +306,32 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     // (unless the caller packed them once)
     if (!packed) launch_pack_scales(s, S1, S2, ws + L.s1t, ws + L.s2t, stream);
     prof_mark(pc, MOE_STAGE_WEIGHT_SCALES, stream);
-    int rc = run_routing(s, L, topk_idx, topk_w, ws, counts, offsets, pool_src, slot_to_pool,
-                         pool_w, stream, pc);
+    int rc = run_routing(s, L, topk_idx, topk_w, ws, pool_tok, counts, offsets, pool_src,
+                         slot_to_pool, pool_w, stream, pc);
     if (rc) return rc;
     if (o.debug_validate && (rc = check_routing_flag(ws, L, stream))) return rc;
 
     uint8_t* tok_s = ws + L.tok_s;
+    // every token row quantised once, token-major; the L1 GEMM gathers the
+    // rows of its tiles through pool_tok
     hipLaunchKernelGGL(k_dispatch_fp8, dim3(T), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(x), H, K, slot_to_pool, pool_q,
-                       static_cast<uint8_t*>(nullptr), tok_s);
+                       static_cast<const uint16_t*>(x), H, K, static_cast<const int32_t*>(nullptr),
+                       x_q, static_cast<uint8_t*>(nullptr), tok_s);
     hipLaunchKernelGGL(k_pool_scales, dim3((unsigned)((L.cap + 255) / 256)), dim3(256), 0,
-                       stream, reinterpret_cast<const uint32_t*>(tok_s), H / 128, pool_src, offsets,
-                       s->E, K, (int64_t)L.cap, reinterpret_cast<uint32_t*>(pool_s));
+                       stream, reinterpret_cast<const uint32_t*>(tok_s), H / 128, pool_tok, offsets,
+                       s->E, (int64_t)L.cap, reinterpret_cast<uint32_t*>(pool_s));
     prof_mark(pc, MOE_STAGE_DISPATCH, stream);
 
     GemmArgs g1;
     memset(&g1, 0, sizeof g1);
-    g1.A = pool_q;
+    g1.A = x_q;
     g1.SA = pool_s;
     g1.B = W1q;
     g1.SB = s1t;
     g1.sa_step = 4 * L.cap;
+    g1.act_s_step = 4 * L.cap;
+    g1.pool_tok = pool_tok;
+    g1.T = T;
     g1.mtiles = reinterpret_cast<const MTile*>(ws + L.mtiles);
     g1.num_mtiles = reinterpret_cast<const int32_t*>(ws + L.num_mtiles);
     g1.Kdim = H;
@@ -337,6 +349,8 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     GemmArgs g2 = g1;
     g2.A = act_q;
     g2.SA = act_s;
+    g2.sa_step = 4 * L.cap;  // packed k-major words of the pool rows
+    g2.pool_tok = nullptr;
     g2.B = W2q;
     g2.SB = s2t;
     g2.Kdim = I;
@@ -431,7 +445,7 @@ int moe_dispatch(const moe_shape_t* s, const void* x, const int64_t* topk_idx, c
         return MOE_ERR_INVALID_ARG;
     if (!device_ok()) return MOE_ERR_DEVICE;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    int rc = run_routing(s, L, topk_idx, topk_w, ws, counts, offsets, pool_src, slot_to_pool,
+    int rc = run_routing(s, L, topk_idx, topk_w, ws, nullptr, counts, offsets, pool_src, slot_to_pool,
                          pool_w, stream);
     if (rc) return rc;
     if (payload == MOE_PAYLOAD_FP8_E4M3)

@@ -82,6 +82,21 @@ __device__ __forceinline__ int b_row_narrow(int nt, int nrow, int I) {
 // Tiles with at most this many rows run narrow.
 constexpr int kNarrowRows = 64;
 
+// Per-lane offsets of a wave's eight A loads and its A-scale load (named
+// fields, so that they stay in registers: an array indexed through the load
+// helpers ends up in scratch memory).
+struct LoadOffs {
+    uint32_t a0, a1, a2, a3, a4, a5, a6, a7, sa;
+    __device__ __forceinline__ uint32_t a(int p) const {
+        return p == 0 ? a0 : p == 1 ? a1 : p == 2 ? a2 : p == 3 ? a3 : p == 4 ? a4 : p == 5 ? a5
+             : p == 6 ? a6 : a7;
+    }
+    __device__ __forceinline__ void set_a(int p, uint32_t v) {
+        if (p == 0) a0 = v; else if (p == 1) a1 = v; else if (p == 2) a2 = v; else if (p == 3) a3 = v;
+        else if (p == 4) a4 = v; else if (p == 5) a5 = v; else if (p == 6) a6 = v; else a7 = v;
+    }
+};
+
 // MFMA operands of one 64-wide K sub-step for one wave: A fragments of its 2
 // row tiles, B fragments of the 8 column tiles.
 struct SubFrags {
@@ -191,7 +206,7 @@ __device__ __forceinline__ int late_copy(int v) {
 template <int MODE>
 __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0, uint8_t* st1,
                                                 uint8_t* st2, float* s_wa, float* s_wb,
-                                                MTile* s_tiles) {
+                                                MTile* s_tiles, int32_t* s_tok) {
     const int tid = threadIdx.x;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int lane = tid & 63;
@@ -255,9 +270,11 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     const uint32_t b_off = (uint32_t)((b_row<MODE>(0, (tid >> 2), g.I) - b_row<MODE>(0, 0, g.I)) * b_ld + 16 * b_chunk);
     // per-load lane offsets (in vector registers: the scalar registers hold
     // one base per operand, advanced by K each step)
-    const uint32_t a_off0 = a_off, a_off1 = a_off + 32 * Kdim, a_off2 = a_off + 64 * Kdim,
-                   a_off3 = a_off + 96 * Kdim, a_off4 = a_off + 128 * Kdim, a_off5 = a_off + 160 * Kdim,
-                   a_off6 = a_off + 192 * Kdim, a_off7 = a_off + 224 * Kdim;
+    // (L1 gathers its A rows from token rows: there the offsets change per
+    // tile, see gather_offsets)
+    LoadOffs lo;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) lo.set_a(p, a_off + 32 * p * Kdim);
     const uint32_t b_off0 = b_off,
                    b_off1 = b_off + (b_row<MODE>(0, 64, g.I) - b_row<MODE>(0, 0, g.I)) * b_ld,
                    b_off2 = b_off + (b_row<MODE>(0, 128, g.I) - b_row<MODE>(0, 0, g.I)) * b_ld,
@@ -269,7 +286,8 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     // lane column p/8, so a lane's eight words are adjacent.  Thread tid loads
     // LDS word tid of each, so it picks its source row accordingly.
     const int64_t sa_step = g.sa_step;
-    const uint32_t sa_off = (uint32_t)(4 * ((tid & ~63) + 32 * (tid & 1) + ((tid & 63) >> 1)));
+    const int sa_row = (tid & ~63) + 32 * (tid & 1) + ((tid & 63) >> 1);
+    lo.sa = (uint32_t)(4 * sa_row);
     const int64_t sb_step = (int64_t)g.N * 4;
     const uint32_t sb_off = (uint32_t)((b_row<MODE>(0, 32 * (tid & 7) + (tid >> 3), g.I) - b_row<MODE>(0, 0, g.I)) * 4);
     // the same lane offsets for the column order of narrow tiles
@@ -286,12 +304,36 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     const uint8_t *a_base, *b_base, *sa_base, *sb_base;
     auto set_bases = [&]() __attribute__((always_inline)) {
         const int b_r0 = b_row<MODE>(nt, 0, g.I);
-        a_base = g.A + (int64_t)row0 * Kdim;
+        a_base = MODE == kL1 ? g.A : g.A + (int64_t)row0 * Kdim;
         b_base = g.B + ((int64_t)e * g.N + b_r0) * b_ld;
         sa_base = g.SA + (int64_t)row0 * 4;
         sb_base = g.SB + (int64_t)e * (Kdim / 128) * sb_step + (int64_t)b_r0 * 4;
     };
     set_bases();
+    // L1: pool row r of a tile reads A row pool_tok[row0 + r] (the
+    // token-major quantised input), so the per-load lane offsets follow the
+    // tile: load p covers tile rows 32p + tid/8.  (The A-scale words are
+    // gathered into pool order beforehand: read scattered, 4 bytes a row,
+    // they would cost as much L2 traffic as the codes.)  Token indices are
+    // clamped to T-1, so rows past the routed ones (whose entries hold
+    // anything) still read inside the buffer.  The offsets are 32-bit: the
+    // host checks T * Kdim < 2^32.
+    const uint32_t tmax = (uint32_t)(g.T - 1);
+    auto gather_offsets = [&](auto tok_at, LoadOffs& o) __attribute__((always_inline)) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+            o.set_a(p, min((uint32_t)tok_at((tid >> 3) + 32 * p), tmax) * (uint32_t)Kdim + 16u * (uint32_t)a_chunk);
+    };
+    LoadOffs nlo = lo;  // the next tile's (L1)
+    if constexpr (MODE == kL1) {
+        const int32_t* tk = g.pool_tok + row0;
+        gather_offsets([&](int r) { return tk[r]; }, lo);
+        // consume them here: the compiler's wait for these loads then lands
+        // before the pipeline starts, not at their first use inside the K
+        // loop (where it would also wait for the direct loads in flight)
+        asm volatile("" ::"v"(lo.a0), "v"(lo.a1), "v"(lo.a2), "v"(lo.a3), "v"(lo.a4), "v"(lo.a5),
+                     "v"(lo.a6), "v"(lo.a7));
+    }
     // LDS stages of the current step k, of k+1 and of k+2; the rotation runs
     // on across tiles.
     const uint8_t* cur = st0;
@@ -310,19 +352,17 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
         constexpr int NAR = decltype(nar)::value;
         const int k0 = kk * kBK;
         if (p < 8) {
-            const uint32_t off = p == 0 ? a_off0 : p == 1 ? a_off1 : p == 2 ? a_off2 : p == 3 ? a_off3
-                               : p == 4 ? a_off4 : p == 5 ? a_off5 : p == 6 ? a_off6 : a_off7;
             if (NAR == 1 && p >= 2)
-                dma_x1(st + w_dst16 + 4096 * p, a_base + k0, a_off0);
+                dma_x1(st + w_dst16 + 4096 * p, a_base + k0, lo.a0);
             else
-                dma_x4(st + w_dst16 + 4096 * p, a_base + k0, off);
+                dma_x4(st + w_dst16 + 4096 * p, a_base + k0, lo.a(p));
         } else if (p < 12) {
             const uint32_t fo = p == 8 ? b_off0 : p == 9 ? b_off1 : p == 10 ? b_off2 : b_off3;
             const uint32_t no = p == 8 ? nb_off0 : p == 9 ? nb_off1 : p == 10 ? nb_off2 : nb_off3;
             const uint32_t off = NAR == 0 ? fo : NAR == 1 ? no : (lnar ? no : fo);
             dma_x4(st + kStageA + w_dst16 + 4096 * (p - 8), b_base + k0 / 2, off);
         } else if (p == 12) {
-            dma_x1(st + kStageA + kStageB + w_dst4, sa_base + kk * sa_step, sa_off);
+            dma_x1(st + kStageA + kStageB + w_dst4, sa_base + kk * sa_step, lo.sa);
         } else if (p == 13) {
             const uint32_t off = NAR == 0 ? sb_off : NAR == 1 ? nsb_off : (lnar ? nsb_off : sb_off);
             dma_x1(st + kStageA + kStageB + kStageSA + w_dst4, sb_base + kk * sb_step, off);
@@ -534,7 +574,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
         // block writes the block's 16 contiguous scale bytes.
         const int I = g.I;
         uint8_t* q_base = g.act_q + (int64_t)row0 * I + nt * 128;                 // wave-uniform
-        uint8_t* s_base = g.act_s + (int64_t)nt * g.sa_step + (int64_t)row0 * 4;  // wave-uniform
+        uint8_t* s_base = g.act_s + (int64_t)nt * g.act_s_step + (int64_t)row0 * 4;  // wave-uniform
         const __amdgpu_buffer_rsrc_t q_rs = rows_rsrc(q_base, nrows * I);
         const __amdgpu_buffer_rsrc_t s_rs = rows_rsrc(s_base, nrows * 4);
         const int rsel = l32 & 7;
@@ -656,7 +696,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
             // group wid spans the 32 lanes of a half-wave (one row each)
             const int I = g.I;
             uint8_t* q_base = g.act_q + (int64_t)row0 * I + nt * 128 + 32 * wid;      // wave-uniform
-            uint8_t* s_base = g.act_s + (int64_t)nt * g.sa_step + (int64_t)row0 * 4;  // wave-uniform
+            uint8_t* s_base = g.act_s + (int64_t)nt * g.act_s_step + (int64_t)row0 * 4;  // wave-uniform
             const __amdgpu_buffer_rsrc_t q_rs = rows_rsrc(q_base, nrows * I);
             const __amdgpu_buffer_rsrc_t s_rs = rows_rsrc(s_base, nrows * 4);
             const int gbyte = ((wid & 1) << 1) | (wid >> 1);  // group wid in the word's byte order
@@ -766,6 +806,34 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
         next = third;
         third = t;
     };
+    // L1: the next tile's token indices arrive in s_tok by a direct load
+    // issued at this tile's start (below).  Every wave has waited for its
+    // own by the barrier of step 1 (the loads of step 3 are the newest 14
+    // then), so from step 2 on any wave may read them; with nk = 3 or 4 the
+    // loop reaches its last three steps before that, and one extra wait
+    // stands in.  Reading them gives the next tile's load offsets, which take
+    // over where the scalar bases switch.
+    auto prep_next_offsets = [&]() __attribute__((always_inline)) {
+        if constexpr (MODE == kL1) {
+            if (nk == 3)
+                barrier_after_vmcnt0();
+            else if (nk == 4)
+                barrier_after_vmcnt14();
+            gather_offsets([&](int r) { return s_tok[r]; }, nlo);
+        }
+    };
+    auto switch_offsets = [&](bool sw) __attribute__((always_inline)) {
+        if constexpr (MODE == kL1) {
+            lo.a0 = sw ? nlo.a0 : lo.a0;
+            lo.a1 = sw ? nlo.a1 : lo.a1;
+            lo.a2 = sw ? nlo.a2 : lo.a2;
+            lo.a3 = sw ? nlo.a3 : lo.a3;
+            lo.a4 = sw ? nlo.a4 : lo.a4;
+            lo.a5 = sw ? nlo.a5 : lo.a5;
+            lo.a6 = sw ? nlo.a6 : lo.a6;
+            lo.a7 = sw ? nlo.a7 : lo.a7;
+        }
+    };
     // The K loop, for a wave with ACT row tiles holding rows; every variant
     // issues the same loads and meets the same barriers.
     auto k_loop = [&](auto act) __attribute__((always_inline)) {
@@ -805,6 +873,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                 }
                 rotate();
             }
+            prep_next_offsets();
             const MTile nrec = s_tiles[more ? tile_i + 1 : tile_i];
             const int n_e = __builtin_amdgcn_readfirstlane(nrec.expert);
             const int n_row0 = __builtin_amdgcn_readfirstlane(nrec.row0);
@@ -827,6 +896,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                         nt = sw ? n_nt : nt;
                         lnar = sw ? (n_nrows <= kNarrowRows ? 1 : 0) : lnar;
                         set_bases();
+                        switch_offsets(sw);
                     }
                     read_piece(Y, cur, 1, g, act);
                     issue_spread(dst2, s2, 1, g, nar_sel);
@@ -918,6 +988,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                 }
                 rotate();
             }
+            prep_next_offsets();
             const MTile nrec = s_tiles[more ? tile_i + 1 : tile_i];
             const int n_e = __builtin_amdgcn_readfirstlane(nrec.expert);
             const int n_row0 = __builtin_amdgcn_readfirstlane(nrec.row0);
@@ -944,6 +1015,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                     nt = sw ? n_nt : nt;
                     lnar = sw ? (n_nrows <= kNarrowRows ? 1 : 0) : lnar;
                     set_bases();
+                    switch_offsets(sw);
                 }
                 barrier_after_vmcnt14();
                 __builtin_amdgcn_sched_barrier(0);
@@ -988,6 +1060,11 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     const int c_row0 = row0, c_nrows = nrows, c_nt = nt;
     const bool c_narrow = nrows <= kNarrowRows;
+    if constexpr (MODE == kL1) {
+        // the next tile's token indices (this tile's again on the last one)
+        const int nrow0 = __builtin_amdgcn_readfirstlane(s_tiles[more ? tile_i + 1 : tile_i].row0);
+        dma_x1(lds_addr(s_tok) + w_dst4, g.pool_tok + nrow0, (uint32_t)(tid * 4));
+    }
     // (L2 only: a short L1 tile is bound by its loads, and the variants cost
     // the L1 kernel registers)
     const int nact = MODE == kL1 ? 2 : (nrows > 64 * wm + 32 ? 2 : (nrows > 64 * wm ? 1 : 0));
@@ -1015,6 +1092,11 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
         take(s_tiles[tile_i + 1]);
         set_bases();
         lnar = nrows <= kNarrowRows ? 1 : 0;
+        if constexpr (MODE == kL1) {
+            // the K loop's barriers have waited for the token indices
+            gather_offsets([&](int r) { return s_tok[r]; }, nlo);
+            switch_offsets(true);
+        }
         lds_reads_done_barrier();
         prologue(s_w_next);
     }
@@ -1051,7 +1133,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_l1(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) uint8_t st2[kStageBytes];
     __shared__ float s_w[2][kBM];
     __shared__ MTile s_tiles[kTileCache];
-    gemm_persistent<kL1>(args, st0, st1, st2, s_w[0], s_w[1], s_tiles);
+    __shared__ int32_t s_tok[kBM];
+    gemm_persistent<kL1>(args, st0, st1, st2, s_w[0], s_w[1], s_tiles, s_tok);
 }
 
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_l2(GemmArgs args) {
@@ -1059,7 +1142,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_l2(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) uint8_t st1[kStageBytes];
     __shared__ __attribute__((aligned(16))) uint8_t st2[kStageBytes];
     __shared__ MTile s_tiles[kTileCache];
-    gemm_persistent<kL2>(args, st0, st1, st2, nullptr, nullptr, s_tiles);
+    gemm_persistent<kL2>(args, st0, st1, st2, nullptr, nullptr, s_tiles, nullptr);
 }
 
 }  // namespace moe

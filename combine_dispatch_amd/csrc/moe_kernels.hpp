@@ -39,11 +39,15 @@ constexpr int kTileCache = 256;
 // byte order (4w, 4w+2, 4w+1, 4w+3), and the words of one K step are stored
 // contiguously over rows: word (w, row) at byte 4 * (w * rows_total + row).
 struct GemmArgs {
-    const uint8_t* A;    // e4m3 [rows][Kdim]
+    const uint8_t* A;    // e4m3 [rows][Kdim]; L1: token rows [T][Kdim] (see pool_tok)
     const uint8_t* SA;   // packed k-major words [Kdim/128][cap rows]
     const uint8_t* B;    // e2m1x2 [E][N][Kdim/2]
     const uint8_t* SB;   // packed k-major words per expert [E][Kdim/128][N]
     int64_t sa_step;     // bytes between K steps of SA (4 * cap)
+    // L1: pool row r takes A row pool_tok[r] (entries past the routed rows may
+    // hold anything: they are clamped to T-1)
+    const int32_t* pool_tok;
+    int32_t T;
     const MTile* mtiles;
     const int32_t* num_mtiles;
     int32_t Kdim;        // reduction size
@@ -52,7 +56,8 @@ struct GemmArgs {
     // L1 epilogue
     const float* pool_w; // [rows]
     uint8_t* act_q;      // e4m3 [rows][I]
-    uint8_t* act_s;      // packed k-major words [I/128][cap], step sa_step
+    uint8_t* act_s;      // packed k-major words [I/128][cap], step act_s_step
+    int64_t act_s_step;  // 4 * cap
     int32_t I;
     int32_t fast_math;
     // L2 epilogue
@@ -68,16 +73,17 @@ __global__ void k_route_scan(const int32_t* __restrict__ seg_hist,
                              int32_t* __restrict__ num_mtiles, int32_t* __restrict__ err_flag);
 __global__ void k_route_scatter(const int64_t* __restrict__ topk_idx,
                                 const float* __restrict__ topk_w, int64_t TK, int E, int nbits,
-                                const int32_t* __restrict__ seg_base,
+                                int K, const int32_t* __restrict__ seg_base,
                                 int32_t* __restrict__ pool_src,
-                                int32_t* __restrict__ slot_to_pool, float* __restrict__ pool_w);
+                                int32_t* __restrict__ slot_to_pool, float* __restrict__ pool_w,
+                                int32_t* __restrict__ pool_tok);
 __global__ void k_dispatch_fp8(const uint16_t* __restrict__ x, int H, int K,
                                const int32_t* __restrict__ slot_to_pool,
                                uint8_t* __restrict__ pool, uint8_t* __restrict__ pool_s,
                                uint8_t* __restrict__ tok_s);
 __global__ void k_pool_scales(const uint32_t* __restrict__ tok_s, int W,
-                              const int32_t* __restrict__ pool_src,
-                              const int32_t* __restrict__ offsets, int E, int K, int64_t cap,
+                              const int32_t* __restrict__ pool_tok,
+                              const int32_t* __restrict__ offsets, int E, int64_t cap,
                               uint32_t* __restrict__ pool_s);
 __global__ void k_scales_kmajor(const uint32_t* __restrict__ S, uint32_t* __restrict__ St, int N,
                                 int W);

@@ -162,8 +162,8 @@ __global__ __launch_bounds__(1024) void k_route_scan(
 // ascending flat-slot order inside every expert.
 __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(
     const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int64_t TK, int E,
-    int nbits, const int32_t* __restrict__ seg_base, int32_t* __restrict__ pool_src,
-    int32_t* __restrict__ slot_to_pool, float* __restrict__ pool_w) {
+    int nbits, int K, const int32_t* __restrict__ seg_base, int32_t* __restrict__ pool_src,
+    int32_t* __restrict__ slot_to_pool, float* __restrict__ pool_w, int32_t* __restrict__ pool_tok) {
     extern __shared__ int32_t lds_run[];  // [kRouteWaves][E]
     const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t nseg = (TK + kSegSlots - 1) / kSegSlots;
@@ -199,6 +199,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(
             pool_src[r] = (int32_t)f;
             slot_to_pool[f] = r;
             pool_w[r] = w;
+            if (pool_tok) pool_tok[r] = (int32_t)(f / K);
             if ((peers >> lane) == 1ull) run[e] = base + __popcll(peers);  // highest peer lane
         } else if (f < TK) {
             slot_to_pool[f] = -1;
@@ -209,9 +210,12 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(
 // a4: gather + quantise.  One block per token row.  Each lane owns 8
 // consecutive columns (one 16-byte load), a quad of lanes owns one 32-column
 // scale group: amax over the quad, UE8M0 scale, e4m3 codes, then the 8 code
-// bytes go to every valid pool row of the token.  The scale bytes go either
-// to every pool row of the token (pool_s, [rows][H/32]) or once to the token
-// (tok_s, [T][H/32]); a null pointer skips that form.
+// bytes go to every valid pool row of the token -- or, with a null
+// slot_to_pool, once to row t of a token-major copy (the fused layer's L1
+// reads token rows from it directly).  The scale bytes go either to every
+// pool row of the token (pool_s, [rows][H/32]) or once to the token (tok_s,
+// [T][H/128] words holding groups 4w, 4w+2, 4w+1, 4w+3 in byte order, the
+// word form the GEMM loads); a null pointer skips that form.
 __global__ __launch_bounds__(256) void k_dispatch_fp8(const uint16_t* __restrict__ x, int H,
                                                      int K, const int32_t* __restrict__ slot_to_pool,
                                                      uint8_t* __restrict__ pool,
@@ -219,7 +223,12 @@ __global__ __launch_bounds__(256) void k_dispatch_fp8(const uint16_t* __restrict
                                                      uint8_t* __restrict__ tok_s) {
     __shared__ int32_t rows[64];
     const int64_t t = blockIdx.x;
-    if (threadIdx.x < K) rows[threadIdx.x] = slot_to_pool[t * K + threadIdx.x];
+    if (!slot_to_pool) {
+        K = 1;
+        if (threadIdx.x == 0) rows[0] = (int32_t)t;
+    } else if (threadIdx.x < K) {
+        rows[threadIdx.x] = slot_to_pool[t * K + threadIdx.x];
+    }
     __syncthreads();
     const uint16_t* xr = x + t * H;
     for (int c0 = threadIdx.x * 8; c0 < H; c0 += 256 * 8) {
@@ -234,7 +243,10 @@ __global__ __launch_bounds__(256) void k_dispatch_fp8(const uint16_t* __restrict
         uint2 q;
         q.x = pack_fp8x4(unscale(f[0], b), unscale(f[1], b), unscale(f[2], b), unscale(f[3], b));
         q.y = pack_fp8x4(unscale(f[4], b), unscale(f[5], b), unscale(f[6], b), unscale(f[7], b));
-        if (tok_s && (threadIdx.x & 3) == 0) tok_s[t * (H / 32) + c0 / 32] = (uint8_t)b;
+        if (tok_s && (threadIdx.x & 3) == 0) {
+            const int gi = c0 / 32;  // group gi is byte (0, 2, 1, 3)[gi % 4] of word gi / 4
+            tok_s[t * (H / 32) + (gi & ~3) + (((gi & 1) << 1) | ((gi >> 1) & 1))] = (uint8_t)b;
+        }
         for (int k = 0; k < K; ++k) {
             const int32_t r = rows[k];
             if (r < 0) continue;
@@ -244,30 +256,30 @@ __global__ __launch_bounds__(256) void k_dispatch_fp8(const uint16_t* __restrict
     }
 }
 
-// Pool scales in packed k-major words (the layout the GEMM loads per K step,
-// bytes in the order 0, 2, 1, 3): word (w, r) = word w of token
-// pool_src[r] / K's scale row.  Thread per pool row: the token's row is read
-// as 16-byte pieces, and for each w consecutive threads write consecutive
-// words.  Rows from R on are left as they are.
+// A-scale words of the pool rows in packed k-major order (the layout the L1
+// GEMM loads per K step: word (w, r) at 4 * (w * cap + r)), gathered from the
+// token-major words the dispatch wrote (already in the byte order 0, 2, 1,
+// 3): word (w, r) = word w of token pool_tok[r].  Thread per pool row; the
+// token's words are read as 16-byte pieces, and for each w consecutive threads
+// write consecutive words.  Rows from R on are left as they are.
 __global__ __launch_bounds__(256) void k_pool_scales(const uint32_t* __restrict__ tok_s, int W,
-                                                    const int32_t* __restrict__ pool_src,
+                                                    const int32_t* __restrict__ pool_tok,
                                                     const int32_t* __restrict__ offsets, int E,
-                                                    int K, int64_t cap,
-                                                    uint32_t* __restrict__ pool_s) {
+                                                    int64_t cap, uint32_t* __restrict__ pool_s) {
     const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (r >= offsets[E]) return;
-    const int64_t t = pool_src[r] / K;
+    const int64_t t = pool_tok[r];
     if ((W & 3) == 0) {
         const uint4* src = reinterpret_cast<const uint4*>(tok_s + t * W);
         for (int w4 = 0; w4 < W / 4; ++w4) {
             const uint4 v = src[w4];
-            pool_s[(int64_t)(4 * w4 + 0) * cap + r] = swap_bytes12(v.x);
-            pool_s[(int64_t)(4 * w4 + 1) * cap + r] = swap_bytes12(v.y);
-            pool_s[(int64_t)(4 * w4 + 2) * cap + r] = swap_bytes12(v.z);
-            pool_s[(int64_t)(4 * w4 + 3) * cap + r] = swap_bytes12(v.w);
+            pool_s[(int64_t)(4 * w4 + 0) * cap + r] = v.x;
+            pool_s[(int64_t)(4 * w4 + 1) * cap + r] = v.y;
+            pool_s[(int64_t)(4 * w4 + 2) * cap + r] = v.z;
+            pool_s[(int64_t)(4 * w4 + 3) * cap + r] = v.w;
         }
     } else {
-        for (int w = 0; w < W; ++w) pool_s[(int64_t)w * cap + r] = swap_bytes12(tok_s[t * W + w]);
+        for (int w = 0; w < W; ++w) pool_s[(int64_t)w * cap + r] = tok_s[t * W + w];
     }
 }
 

@@ -106,7 +106,7 @@ size_t moe_dispatch_workspace_bytes(const moe_shape_t* s);
  * fp32, requantised the same way per 32 along I; combine sums the slots' bf16
  * rows in fp32 in ascending k, then rounds to bf16.
  * Shapes: H % 256 == 0, I % 128 == 0, 1 <= E <= 1024, 1 <= K <= 64,
- * T * K < 2^31.  Otherwise MOE_ERR_UNSUPPORTED.
+ * T * K < 2^31, T * H < 2^32.  Otherwise MOE_ERR_UNSUPPORTED.
  */
 int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt /* NULL = defaults */,
                       const void* x, const int64_t* topk_idx, const float* topk_w,
@@ -184,16 +184,22 @@ int moe_combine(const moe_shape_t* s, const void* pool_out, const int32_t* slot_
                 const float* topk_w, void* y, moe_stream_t stream);
 
 /* Byte offsets of intermediates inside a moe_fused_forward workspace, so that
- * tests can read them after a call (all -1 on a bad shape). */
-/* The block scales of the pool and of the activation are stored as packed
- * k-major words: the word for row r and K step w (128 columns) holds the
- * UE8M0 bytes of the row's 32-column groups 4w, 4w+2, 4w+1, 4w+3 (in that
- * byte order) at byte offset 4 * (w * cap + r), so one K step of a row tile
- * is one contiguous run (the pages' SF buffers pack 4 UE8M0 per 128
- * columns, [P3] appendix A.1). */
+ * tests can read them after a call (all -1 on a bad shape).
+ * The fused layer quantises every token row once (x_q, token-major) and its
+ * L1 GEMM reads pool row r from token row pool_tok[r]; the expert-major pool
+ * itself is not materialised (moe_dispatch materialises it).
+ * Block scales are stored as 4-byte words of four UE8M0 bytes, one word per
+ * row and 128-column K step w, holding the row's 32-column groups 4w, 4w+2,
+ * 4w+1, 4w+3 in that byte order (the pages' SF buffers pack 4 UE8M0 per 128
+ * columns, [P3] appendix A.1): for x_s token-major, word (t, w) at byte
+ * 4 * (t * H/128 + w); for pool_s and act_s packed k-major, word (r, w) at
+ * byte 4 * (w * cap + r), so that one K step of a row tile is one contiguous
+ * run. */
 typedef struct {
     int64_t counts, offsets, pool_src, slot_to_pool, pool_w; /* routing arrays */
-    int64_t pool_q, pool_s;   /* e4m3 [cap][H], packed k-major words [H/128][cap] */
+    int64_t pool_tok;         /* int32 [cap]: token of pool row r (first R entries) */
+    int64_t x_q, x_s;         /* e4m3 [T][H], words [T][H/128] */
+    int64_t pool_s;           /* x_s words of the pool rows, packed k-major [H/128][cap] */
     int64_t act_q, act_s;     /* e4m3 [cap][I], packed k-major words [I/128][cap] */
     int64_t l2_out;           /* bf16 [cap][H] */
     int64_t capacity_rows;    /* cap = T*K + tile padding */

@@ -47,12 +47,17 @@ def view(workspace: torch.Tensor, inp: dict, name: str, rows: int | None = None)
     spec = {
         "counts": (np.int32, (E,)), "offsets": (np.int32, (E + 1,)),
         "pool_src": (np.int32, (TK,)), "slot_to_pool": (np.int32, (TK,)),
-        "pool_w": (np.float32, (TK,)), "pool_q": (np.uint8, (TK, H)),
+        "pool_w": (np.float32, (TK,)), "pool_tok": (np.int32, (TK,)),
+        "x_q": (np.uint8, (T, H)), "x_s": (np.uint8, (T, H // 32)),
         "pool_s": (np.uint8, (TK, H // 32)), "act_q": (np.uint8, (TK, I)),
         "act_s": (np.uint8, (TK, I // 32)), "l2_out": (np.uint16, (TK, H)),
     }
     dt, shape = spec[name]
     off = v[name]
+    if name == "x_s":
+        # token-major words, bytes = groups 4w, 4w+2, 4w+1, 4w+3
+        raw = workspace[off:off + T * (H // 32)].cpu().numpy()
+        return np.ascontiguousarray(raw.reshape(T, H // 128, 4)[:, :, [0, 2, 1, 3]].reshape(T, H // 32))
     if name in ("pool_s", "act_s"):
         # packed k-major words: word (w, r) at 4 * (w * cap + r), bytes = groups
         # 4w, 4w+2, 4w+1, 4w+3

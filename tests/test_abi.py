@@ -59,8 +59,8 @@ def test_workspace_sizing(moe):
     T, H, I, E, K = 8192, 7168, 2048, 32, 8
     b = moe.moe_workspace_bytes(T, H, I, E, K)
     cap = T * K + 256
-    # pool e4m3 + scales, act e4m3 + scales, L2 bf16 rows: the bulk of it
-    bulk = cap * (H + H // 32 + I + I // 32 + 2 * H)
+    # token rows e4m3 + scales, act e4m3 + scales, L2 bf16 rows: the bulk of it
+    bulk = T * (H + H // 32) + cap * (I + I // 32 + 2 * H)
     assert bulk <= b <= bulk + 64 * 1024 * 1024
     v = moe.moe_workspace_views(T, H, I, E, K)
     assert v["capacity_rows"] == cap

@@ -2,8 +2,9 @@
 same seeded inputs.
 
 Bars (routing and dispatch are integer/byte work, the rest floating point):
-  - counts, offsets, pool_src, slot_to_pool, pool_w, pool codes and pool
-    scale bytes: bit-exact;
+  - counts, offsets, pool_src, slot_to_pool, pool_w, the token of each pool
+    row, and the quantised token rows (codes and scale bytes) the L1 GEMM
+    gathers its pool rows from: bit-exact;
   - combine fed identical bf16 rows: bit-exact (same summation order);
   - intermediate FP8 activations after L1: scale bytes and codes identical
     except at most 0.1% of elements, which may be one code step apart (one
@@ -117,7 +118,11 @@ def test_forward_matches_oracle_small(case):
     y_ref, mid = oracle.forward(inp, intermediates=True)
     y, ws = run_forward(inp)
     r, R = check_routing(inp, ws)
-    np.testing.assert_array_equal(view(ws, inp, "pool_q", R), mid["pool_q"][:R])
+    # pool row r is token row pool_tok[r] of the quantised input
+    ptok = view(ws, inp, "pool_tok", R)
+    np.testing.assert_array_equal(ptok, r["pool_src"][:R] // inp["K"])
+    np.testing.assert_array_equal(view(ws, inp, "x_q")[ptok], mid["pool_q"][:R])
+    np.testing.assert_array_equal(view(ws, inp, "x_s")[ptok], mid["pool_s"][:R])
     np.testing.assert_array_equal(view(ws, inp, "pool_s", R), mid["pool_s"][:R])
     check_act(view(ws, inp, "act_q", R), view(ws, inp, "act_s", R), mid["act_q"][:R],
               mid["act_s"][:R])
@@ -132,8 +137,9 @@ def test_forward_is_deterministic():
     y2, ws2 = run_forward(inp, dev)
     np.testing.assert_array_equal(y1, y2)
     R = int(view(ws1, inp, "offsets")[-1])
-    for name in ("pool_src", "pool_q", "act_q", "act_s", "l2_out"):  # rows past R are scratch
+    for name in ("pool_src", "pool_tok", "act_q", "act_s", "l2_out"):  # rows past R are scratch
         np.testing.assert_array_equal(view(ws1, inp, name, R), view(ws2, inp, name, R))
+    np.testing.assert_array_equal(view(ws1, inp, "x_q"), view(ws2, inp, "x_q"))
 
 
 # ----------------------------------------------------------------------------
@@ -313,16 +319,18 @@ def test_full_size_workload(name):
     y, ws = run_forward(inp)
     r, R = check_routing(inp, ws)
     say("routing bit-exact, R =", R)
-    # pool bytes of sampled rows against the oracle's quantisation of the token row
+    # the quantised token rows behind sampled pool rows against the oracle
     rng = np.random.default_rng(7)
     rows = np.unique(np.concatenate([rng.integers(0, R, 256), [0, R - 1]]))
-    pq, ps = view(ws, inp, "pool_q", R)[rows], view(ws, inp, "pool_s", R)[rows]
     K, H = inp["K"], inp["H"]
-    for i, rr in enumerate(rows):
+    ptok = view(ws, inp, "pool_tok", R)
+    np.testing.assert_array_equal(ptok, r["pool_src"][:R] // K)
+    xq, xs = view(ws, inp, "x_q"), view(ws, inp, "x_s")
+    for rr in rows:
         t = r["pool_src"][rr] // K
         q, s = oracle.quant_e4m3_row(oracle.bf16_to_f32(inp["x"][t]))
-        np.testing.assert_array_equal(pq[i], q)
-        np.testing.assert_array_equal(ps[i], s)
+        np.testing.assert_array_equal(xq[t], q)
+        np.testing.assert_array_equal(xs[t], s)
     # y on sampled tokens (including any fully masked one) against brute force
     masked = np.nonzero((inp["topk_idx"] < 0).all(axis=1))[0][:2]
     toks = np.unique(np.concatenate([rng.integers(0, inp["T"], 6), [0, inp["T"] - 1], masked]))
