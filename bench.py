@@ -198,8 +198,10 @@ def main():
     l2_flop = 2.0 * R * I * H
     l1_tflops = l1_flop / (per_launch["gemm_l1"] * 1e-3) / 1e12
     l2_tflops = l2_flop / (per_launch["gemm_l2"] * 1e-3) / 1e12
-    # algorithmic bytes of the bandwidth-bound kernels (see the design notes)
-    disp_bytes = T * H * 2 + R * (H + H // 32) + T * K * 8 * 2
+    # algorithmic bytes of the bandwidth-bound kernels (see the design notes):
+    # dispatch = x read, token-major codes and scale words written, the pool
+    # rows' scale words gathered (read and written) by their token index
+    disp_bytes = T * H * 2 + T * (H + H // 32) + 2 * R * (H // 32) + 4 * R
     comb_bytes = R * H * 2 + T * H * 2 + T * K * 4
 
     traffic = measured_traffic(a.workload)
