@@ -371,8 +371,13 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
             for (int u = 0; u < 8; ++u) {
                 const int k = k0 + u;
                 const int32_t r = k < K ? rows[k] : -1;
-                v[u] = r >= 0 ? *reinterpret_cast<const uint4*>(o + (int64_t)r * H + c0)
-                              : make_uint4(0, 0, 0, 0);
+                // streamed: each L2 output byte is read exactly once
+                typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                const u32x4 z = {0, 0, 0, 0};
+                const u32x4 t4 = r >= 0 ? __builtin_nontemporal_load(
+                                              reinterpret_cast<const u32x4*>(o + (int64_t)r * H + c0))
+                                        : z;
+                v[u] = make_uint4(t4.x, t4.y, t4.z, t4.w);
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
