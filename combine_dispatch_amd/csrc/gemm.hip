@@ -544,6 +544,10 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
         const int N = g.N;
         uint8_t* out_base = reinterpret_cast<uint8_t*>(g.out + (int64_t)row0 * N + nt * kBN);  // wave-uniform
         const __amdgpu_buffer_rsrc_t out_rs = rows_rsrc(out_base, nrows * N * 2);
+        // byte offset of row 64*wm + 4*h, columns 8*l32..: each row register
+        // adds a wave-uniform multiple of the row pitch
+        const int lane_off = 2 * ((64 * wm + 4 * h) * N + 8 * l32);
+        const int pitch = 2 * N;
         auto rows = [&](auto partial) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -556,8 +560,8 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                     for (int j = 0; j < 8; ++j) asm("v_accvgpr_read_b32 %0, %1" : "=v"(c[j]) : "a"(acc[i][j][r]));
                     const u32x4 v = {pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]),
                                      pack_bf16x2(c[4], c[5]), pack_bf16x2(c[6], c[7])};
-                    const int lrow = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                    __builtin_amdgcn_raw_buffer_store_b128(v, out_rs, 2 * (lrow * N + 8 * l32), 0, kStoreNT);
+                    const int step = 32 * i + 8 * (r >> 2) + (r & 3);
+                    __builtin_amdgcn_raw_buffer_store_b128(v, out_rs, lane_off + pitch * step, 0, kStoreNT);
                 }
             }
         };
@@ -579,6 +583,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
         const __amdgpu_buffer_rsrc_t s_rs = rows_rsrc(s_base, nrows * 4);
         const int rsel = l32 & 7;
         const uint32_t bshift = 8u * (uint32_t)(rsel & 3);
+        const int q_lane = (64 * wm + 4 * h) * I + 4 * l32;  // row 64*wm + 4*h, this lane's 4 codes
         const int G = l32 >> 3, gbyte = ((G & 1) << 1) | (G >> 1);
         auto rows = [&](auto fast, auto partial) __attribute__((always_inline)) {
             constexpr bool kPartial = decltype(partial)::value;
@@ -653,7 +658,8 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
                     const uint32_t bsel = b4 >> bshift;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr)
-                        __builtin_amdgcn_raw_buffer_store_b32(codes[rr], q_rs, (lrow0 + rr) * I + 4 * l32, 0, kStoreNT);
+                        __builtin_amdgcn_raw_buffer_store_b32(codes[rr], q_rs, q_lane + I * (32 * i + 8 * rq + rr),
+                                                              0, kStoreNT);
                     // group G is byte (0, 2, 1, 3)[G] of the word; lanes with
                     // rsel >= 4 store nothing (an offset past the range)
                     const int s_off = rsel < 4 ? (lrow0 + rsel) * 4 + gbyte : 0x40000000;
