@@ -361,53 +361,63 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
         wts[threadIdx.x] = topk_w ? topk_w[t * K + threadIdx.x] : 1.0f;
     }
     __syncthreads();
-    for (int c0 = threadIdx.x * 8; c0 < H; c0 += 256 * 8) {
-        float acc[8];
+    // Two 2048-column chunks per pass, so that 2K loads per thread are in
+    // flight before the first sum.
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    for (int c00 = threadIdx.x * 8; c00 < H; c00 += 2 * 256 * 8) {
+        float acc[2][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[hh][j] = 0.0f;
         for (int k0 = 0; k0 < K; k0 += 8) {
-            uint4 v[8];
+            u32x4 v[2][8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int k = k0 + u;
-                const int32_t r = k < K ? rows[k] : -1;
-                // streamed: each L2 output byte is read exactly once
-                typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-                const u32x4 z = {0, 0, 0, 0};
-                const u32x4 t4 = r >= 0 ? __builtin_nontemporal_load(
-                                              reinterpret_cast<const u32x4*>(o + (int64_t)r * H + c0))
-                                        : z;
-                v[u] = make_uint4(t4.x, t4.y, t4.z, t4.w);
+            for (int hh = 0; hh < 2; ++hh) {
+                const int c0 = c00 + hh * 256 * 8;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int k = k0 + u;
+                    const int32_t r = (k < K && c0 < H) ? rows[k] : -1;
+                    // streamed: each L2 output byte is read exactly once
+                    const u32x4 z = {0, 0, 0, 0};
+                    v[hh][u] = r >= 0 ? __builtin_nontemporal_load(
+                                            reinterpret_cast<const u32x4*>(o + (int64_t)r * H + c0))
+                                      : z;
+                }
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int k = k0 + u;
-                if (k >= K || rows[k] < 0) continue;
-                const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-                if (topk_w) {
-                    const float wk = wts[k];
+            for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        acc[2 * j] = acc[2 * j] + bf16_lo(w4[j]) * wk;
-                        acc[2 * j + 1] = acc[2 * j + 1] + bf16_hi(w4[j]) * wk;
-                    }
-                } else {
+                for (int u = 0; u < 8; ++u) {
+                    const int k = k0 + u;
+                    if (k >= K || rows[k] < 0) continue;
+                    const uint32_t w4[4] = {v[hh][u].x, v[hh][u].y, v[hh][u].z, v[hh][u].w};
+                    if (topk_w) {
+                        const float wk = wts[k];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        acc[2 * j] = acc[2 * j] + bf16_lo(w4[j]);
-                        acc[2 * j + 1] = acc[2 * j + 1] + bf16_hi(w4[j]);
+                        for (int j = 0; j < 4; ++j) {
+                            acc[hh][2 * j] = acc[hh][2 * j] + bf16_lo(w4[j]) * wk;
+                            acc[hh][2 * j + 1] = acc[hh][2 * j + 1] + bf16_hi(w4[j]) * wk;
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            acc[hh][2 * j] = acc[hh][2 * j] + bf16_lo(w4[j]);
+                            acc[hh][2 * j + 1] = acc[hh][2 * j + 1] + bf16_hi(w4[j]);
+                        }
                     }
                 }
             }
         }
-        uint4 out;
-        out.x = pack_bf16x2(acc[0], acc[1]);
-        out.y = pack_bf16x2(acc[2], acc[3]);
-        out.z = pack_bf16x2(acc[4], acc[5]);
-        out.w = pack_bf16x2(acc[6], acc[7]);
-        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-        __builtin_nontemporal_store(u32x4{out.x, out.y, out.z, out.w},
-                                    reinterpret_cast<u32x4*>(y + t * H + c0));  // streamed out
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int c0 = c00 + hh * 256 * 8;
+            if (c0 >= H) continue;
+            const u32x4 out = {pack_bf16x2(acc[hh][0], acc[hh][1]), pack_bf16x2(acc[hh][2], acc[hh][3]),
+                               pack_bf16x2(acc[hh][4], acc[hh][5]), pack_bf16x2(acc[hh][6], acc[hh][7])};
+            __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(y + t * H + c0));  // streamed out
+        }
     }
 }
 
