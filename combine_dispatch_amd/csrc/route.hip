@@ -361,19 +361,20 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
         wts[threadIdx.x] = topk_w ? topk_w[t * K + threadIdx.x] : 1.0f;
     }
     __syncthreads();
-    // Two 2048-column chunks per pass, so that 2K loads per thread are in
-    // flight before the first sum.
+    // Four 2048-column chunks per pass, so that 4K loads per thread are in
+    // flight before the first sum (the read stream then runs at the rate of
+    // a plain read of HBM).
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    for (int c00 = threadIdx.x * 8; c00 < H; c00 += 2 * 256 * 8) {
-        float acc[2][8];
+    for (int c00 = threadIdx.x * 8; c00 < H; c00 += 4 * 256 * 8) {
+        float acc[4][8];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < 4; ++hh)
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[hh][j] = 0.0f;
         for (int k0 = 0; k0 < K; k0 += 8) {
-            u32x4 v[2][8];
+            u32x4 v[4][8];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
+            for (int hh = 0; hh < 4; ++hh) {
                 const int c0 = c00 + hh * 256 * 8;
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
                 }
             }
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
+            for (int hh = 0; hh < 4; ++hh) {
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const int k = k0 + u;
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
             }
         }
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
+        for (int hh = 0; hh < 4; ++hh) {
             const int c0 = c00 + hh * 256 * 8;
             if (c0 >= H) continue;
             const u32x4 out = {pack_bf16x2(acc[hh][0], acc[hh][1]), pack_bf16x2(acc[hh][2], acc[hh][3]),
