@@ -90,8 +90,15 @@ __global__ void k_scales_kmajor(const uint32_t* __restrict__ S, uint32_t* __rest
 __global__ void k_dispatch_bf16(const uint16_t* __restrict__ x, int H, int K,
                                 const int32_t* __restrict__ slot_to_pool,
                                 uint16_t* __restrict__ pool);
+// Tokens per combine block: as many whole rows as fit 8192 columns (at most
+// kCombineMaxTokens), else one.
+constexpr int kCombineMaxTokens = 32;
+inline int combine_tokens_per_block(int H) {
+    const int t = 8192 / H;
+    return t < 1 ? 1 : (t > kCombineMaxTokens ? kCombineMaxTokens : t);
+}
 __global__ void k_combine(const uint16_t* __restrict__ o, const int32_t* __restrict__ slot_to_pool,
-                          const float* __restrict__ topk_w, int H, int K,
+                          const float* __restrict__ topk_w, int64_t T, int H, int K, int tpb,
                           uint16_t* __restrict__ y);
 __global__ void k_gemm_l1(GemmArgs args);
 __global__ void k_gemm_l2(GemmArgs args);

@@ -344,28 +344,40 @@ __global__ __launch_bounds__(256) void k_dispatch_bf16(const uint16_t* __restric
     }
 }
 
-// a9: combine.  One block per token; each lane owns 8 columns.  The K pool
-// rows of the token are loaded first (independent loads in flight), then
-// summed in ascending k in fp32 starting from +0, then rounded to bf16.
-// Multiplies and adds stay separately rounded.
+// a9: combine.  A block takes tpb consecutive tokens (tpb * H <= 8192 when
+// tpb > 1, so that small rows still fill the block); each lane owns 8
+// columns of up to four 2048-column chunks of the block's flat [tpb][H] span.
+// The K pool rows behind every chunk are loaded first (4K independent loads
+// in flight per lane, the rate of a plain HBM read stream), then summed in
+// ascending k in fp32 starting from +0, then rounded to bf16.  Multiplies and
+// adds stay separately rounded.
 #pragma clang fp contract(off)
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
                                                 const int32_t* __restrict__ slot_to_pool,
-                                                const float* __restrict__ topk_w, int H, int K,
+                                                const float* __restrict__ topk_w, int64_t T,
+                                                int H, int K, int tpb,
                                                 uint16_t* __restrict__ y) {
-    __shared__ int32_t rows[64];
-    __shared__ float wts[64];
-    const int64_t t = blockIdx.x;
-    if (threadIdx.x < K) {
-        rows[threadIdx.x] = slot_to_pool[t * K + threadIdx.x];
-        wts[threadIdx.x] = topk_w ? topk_w[t * K + threadIdx.x] : 1.0f;
+    __shared__ int32_t rows[kCombineMaxTokens * 64];
+    __shared__ float wts[kCombineMaxTokens * 64];
+    const int64_t t0 = (int64_t)blockIdx.x * tpb;
+    for (int i = threadIdx.x; i < tpb * K; i += 256) {
+        const int64_t t = t0 + i / K;
+        const bool in = t < T;
+        rows[i] = in ? slot_to_pool[t0 * K + i] : -1;
+        wts[i] = (in && topk_w) ? topk_w[t0 * K + i] : 1.0f;
     }
     __syncthreads();
-    // Four 2048-column chunks per pass, so that 4K loads per thread are in
-    // flight before the first sum (the read stream then runs at the rate of
-    // a plain read of HBM).
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    for (int c00 = threadIdx.x * 8; c00 < H; c00 += 4 * 256 * 8) {
+    const int span = tpb * H;  // flat columns of the block's tokens
+    for (int c00 = threadIdx.x * 8; c00 < span; c00 += 4 * 256 * 8) {
+        int tok[4], col[4];
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+            const int p = c00 + hh * 256 * 8;
+            const int j = p < span ? p / H : -1;  // H % 8 == 0: a lane's 8 columns share a token
+            tok[hh] = j;
+            col[hh] = j >= 0 ? p - j * H : 0;
+        }
         float acc[4][8];
 #pragma unroll
         for (int hh = 0; hh < 4; ++hh)
@@ -375,27 +387,27 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
             u32x4 v[4][8];
 #pragma unroll
             for (int hh = 0; hh < 4; ++hh) {
-                const int c0 = c00 + hh * 256 * 8;
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const int k = k0 + u;
-                    const int32_t r = (k < K && c0 < H) ? rows[k] : -1;
+                    const int32_t r = (k < K && tok[hh] >= 0) ? rows[tok[hh] * K + k] : -1;
                     // streamed: each L2 output byte is read exactly once
                     const u32x4 z = {0, 0, 0, 0};
-                    v[hh][u] = r >= 0 ? __builtin_nontemporal_load(
-                                            reinterpret_cast<const u32x4*>(o + (int64_t)r * H + c0))
+                    v[hh][u] = r >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                                            o + (int64_t)r * H + col[hh]))
                                       : z;
                 }
             }
 #pragma unroll
             for (int hh = 0; hh < 4; ++hh) {
+                if (tok[hh] < 0) continue;
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const int k = k0 + u;
-                    if (k >= K || rows[k] < 0) continue;
+                    if (k >= K || rows[tok[hh] * K + k] < 0) continue;
                     const uint32_t w4[4] = {v[hh][u].x, v[hh][u].y, v[hh][u].z, v[hh][u].w};
                     if (topk_w) {
-                        const float wk = wts[k];
+                        const float wk = wts[tok[hh] * K + k];
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             acc[hh][2 * j] = acc[hh][2 * j] + bf16_lo(w4[j]) * wk;
@@ -413,11 +425,11 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
         }
 #pragma unroll
         for (int hh = 0; hh < 4; ++hh) {
-            const int c0 = c00 + hh * 256 * 8;
-            if (c0 >= H) continue;
+            if (tok[hh] < 0 || t0 + tok[hh] >= T) continue;
             const u32x4 out = {pack_bf16x2(acc[hh][0], acc[hh][1]), pack_bf16x2(acc[hh][2], acc[hh][3]),
                                pack_bf16x2(acc[hh][4], acc[hh][5]), pack_bf16x2(acc[hh][6], acc[hh][7])};
-            __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(y + t * H + c0));  // streamed out
+            __builtin_nontemporal_store(
+                out, reinterpret_cast<u32x4*>(y + (t0 + tok[hh]) * H + col[hh]));  // streamed out
         }
     }
 }

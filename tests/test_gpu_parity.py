@@ -177,11 +177,18 @@ def test_dispatch_entry_matches_oracle(payload):
         np.testing.assert_array_equal(scales.cpu().numpy()[:R], ref["pool_scales"][:R])
 
 
+# (T, H, K): blocks of 8, 4, 2, 1 and 32 tokens with a ragged last block, a
+# partly used chunk (H = 3072), and a row longer than one pass (H = 16384).
+COMBINE_SHAPES = [(777, 1024, 8), (1001, 2048, 8), (333, 3072, 6), (65, 7168, 8), (130, 40, 64),
+                  (17, 16384, 3)]
+
+
+@pytest.mark.parametrize("shape", COMBINE_SHAPES, ids=lambda s: "T%d_H%d_K%d" % s)
 @pytest.mark.parametrize("weighted", [False, True])
-def test_combine_entry_bit_exact(weighted):
+def test_combine_entry_bit_exact(weighted, shape):
     import combine_dispatch_amd as moe
-    T, H, K = 777, 1024, 8
-    rng = np.random.default_rng(61)
+    T, H, K = shape
+    rng = np.random.default_rng(61 + H)
     R = T * K
     o = (rng.standard_normal((R, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     s2p = rng.permutation(R).astype(np.int32)
