@@ -199,9 +199,11 @@ def main():
     l1_tflops = l1_flop / (per_launch["gemm_l1"] * 1e-3) / 1e12
     l2_tflops = l2_flop / (per_launch["gemm_l2"] * 1e-3) / 1e12
     # algorithmic bytes of the bandwidth-bound kernels (see the design notes):
-    # dispatch = x read, token-major codes and scale words written, the pool
-    # rows' scale words gathered (read and written) by their token index
-    disp_bytes = T * H * 2 + T * (H + H // 32) + 2 * R * (H // 32) + 4 * R
+    # dispatch = x read, token-major codes and scale words written, topk_idx
+    # read by the histogram in the same launch; pool scales = the pool rows'
+    # scale words gathered (read and written) by their token index
+    disp_bytes = T * H * 2 + T * (H + H // 32) + 8 * T * K
+    pool_s_bytes = 2 * R * (H // 32) + 4 * R
     comb_bytes = R * H * 2 + T * H * 2 + T * K * 4
 
     traffic = measured_traffic(a.workload)
@@ -233,6 +235,7 @@ def main():
         "kernels": {
             "gemm_l2_tflops": round(l2_tflops, 2),
             "dispatch_gbs": round(disp_bytes / (per_launch["dispatch"] * 1e-3) / 1e9, 1),
+            "pool_scales_gbs": round(pool_s_bytes / (per_launch["pool_scales"] * 1e-3) / 1e9, 1),
             "combine_gbs": round(comb_bytes / (per_launch["combine"] * 1e-3) / 1e9, 1),
             "hbm_peak_gbs": PEAK_HBM_GBS,
         },

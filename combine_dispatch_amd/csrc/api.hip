@@ -160,19 +160,23 @@ int bits_for(int E) {
 }
 
 // a1-a3 into caller-visible arrays; the segment scratch lives at ws.
+// a1 (unless the caller's first launch already ran it), a2, a3.
+int route_blocks(const Layout& L) { return (int)((L.nseg + kRouteWaves - 1) / kRouteWaves); }
+
 int run_routing(const moe_shape_t* s, const Layout& L, const int64_t* topk_idx, const float* topk_w,
                 uint8_t* ws, int32_t* pool_tok, int32_t* counts, int32_t* offsets, int32_t* pool_src,
-                int32_t* slot_to_pool, float* pool_w, hipStream_t stream, int pc = -1) {
+                int32_t* slot_to_pool, float* pool_w, hipStream_t stream, bool counted,
+                int pc = -1) {
     const int64_t TK = (int64_t)s->T * s->K;
     const int E = s->E;
-    const int nblk = (int)((L.nseg + kRouteWaves - 1) / kRouteWaves);
+    const int nblk = route_blocks(L);
     const size_t lds = sizeof(int32_t) * kRouteWaves * E;
     int32_t* seg_hist = reinterpret_cast<int32_t*>(ws + L.seg_hist);
     int32_t* seg_base = reinterpret_cast<int32_t*>(ws + L.seg_base);
     int32_t* seg_err = reinterpret_cast<int32_t*>(ws + L.seg_err);
-    hipLaunchKernelGGL(k_route_count, dim3(nblk), dim3(kRouteThreads), lds, stream, topk_idx, TK,
-                       E, seg_hist, seg_err);
-    prof_mark(pc, MOE_STAGE_ROUTE_COUNT, stream);
+    if (!counted)
+        hipLaunchKernelGGL(k_route_count, dim3(nblk), dim3(kRouteThreads), lds, stream, topk_idx,
+                           TK, E, seg_hist, seg_err);
     const int scan_threads = 1024;  // several threads per expert split the segments
     hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(scan_threads), 0, stream, seg_hist, seg_err,
                        (int)L.nseg, E, seg_base, counts, offsets,
@@ -306,21 +310,30 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     // (unless the caller packed them once)
     if (!packed) launch_pack_scales(s, S1, S2, ws + L.s1t, ws + L.s2t, stream);
     prof_mark(pc, MOE_STAGE_WEIGHT_SCALES, stream);
+    uint8_t* tok_s = ws + L.tok_s;
+    {
+        // every token row quantised once, token-major (the L1 GEMM gathers the
+        // rows of its tiles through pool_tok); the a1 histogram in the same
+        // launch
+        const int tpb = tokens_per_block(H);
+        const int ncount = route_blocks(L);
+        const int64_t nq = ((int64_t)T + tpb - 1) / tpb;
+        hipLaunchKernelGGL(k_quantise_count, dim3((unsigned)(ncount + nq)), dim3(256),
+                           sizeof(int32_t) * kRouteWaves * s->E, stream,
+                           static_cast<const uint16_t*>(x), (int64_t)T, H, tpb, x_q, tok_s, topk_idx,
+                           (int64_t)T * K, s->E, ncount, reinterpret_cast<int32_t*>(ws + L.seg_hist),
+                           reinterpret_cast<int32_t*>(ws + L.seg_err));
+    }
+    prof_mark(pc, MOE_STAGE_DISPATCH, stream);
     int rc = run_routing(s, L, topk_idx, topk_w, ws, pool_tok, counts, offsets, pool_src,
-                         slot_to_pool, pool_w, stream, pc);
+                         slot_to_pool, pool_w, stream, true, pc);
     if (rc) return rc;
     if (o.debug_validate && (rc = check_routing_flag(ws, L, stream))) return rc;
 
-    uint8_t* tok_s = ws + L.tok_s;
-    // every token row quantised once, token-major; the L1 GEMM gathers the
-    // rows of its tiles through pool_tok
-    hipLaunchKernelGGL(k_dispatch_fp8, dim3(T), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(x), H, K, static_cast<const int32_t*>(nullptr),
-                       x_q, static_cast<uint8_t*>(nullptr), tok_s);
     hipLaunchKernelGGL(k_pool_scales, dim3((unsigned)((L.cap + 255) / 256)), dim3(256), 0,
                        stream, reinterpret_cast<const uint32_t*>(tok_s), H / 128, pool_tok, offsets,
                        s->E, (int64_t)L.cap, reinterpret_cast<uint32_t*>(pool_s));
-    prof_mark(pc, MOE_STAGE_DISPATCH, stream);
+    prof_mark(pc, MOE_STAGE_POOL_SCALES, stream);
 
     GemmArgs g1;
     memset(&g1, 0, sizeof g1);
@@ -362,7 +375,7 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     prof_mark(pc, MOE_STAGE_GEMM_L2, stream);
 
     {
-        const int tpb = combine_tokens_per_block(H);
+        const int tpb = tokens_per_block(H);
         hipLaunchKernelGGL(k_combine, dim3((unsigned)(((int64_t)T + tpb - 1) / tpb)), dim3(256), 0, stream,
                            l2_out, slot_to_pool, static_cast<const float*>(nullptr), (int64_t)T, H,
                            K, tpb, static_cast<uint16_t*>(y));
@@ -450,11 +463,13 @@ int moe_dispatch(const moe_shape_t* s, const void* x, const int64_t* topk_idx, c
     if (!device_ok()) return MOE_ERR_DEVICE;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     int rc = run_routing(s, L, topk_idx, topk_w, ws, nullptr, counts, offsets, pool_src, slot_to_pool,
-                         pool_w, stream);
+                         pool_w, stream, false);
     if (rc) return rc;
+    const int tpb = tokens_per_block(s->H);
     if (payload == MOE_PAYLOAD_FP8_E4M3)
-        hipLaunchKernelGGL(k_dispatch_fp8, dim3(s->T), dim3(256), 0, stream,
-                           static_cast<const uint16_t*>(x), s->H, s->K, slot_to_pool,
+        hipLaunchKernelGGL(k_dispatch_fp8, dim3((unsigned)(((int64_t)s->T + tpb - 1) / tpb)),
+                           dim3(256), 0, stream, static_cast<const uint16_t*>(x), (int64_t)s->T, s->H,
+                           s->K, tpb, slot_to_pool,
                            static_cast<uint8_t*>(pool), pool_scales, static_cast<uint8_t*>(nullptr));
     else
         hipLaunchKernelGGL(k_dispatch_bf16, dim3(s->T), dim3(256), 0, stream,
@@ -471,7 +486,7 @@ int moe_combine(const moe_shape_t* s, const void* pool_out, const int32_t* slot_
     if (!pool_out || !slot_to_pool || !y) return MOE_ERR_INVALID_ARG;
     if (!device_ok()) return MOE_ERR_DEVICE;
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-    const int tpb = combine_tokens_per_block(s->H);
+    const int tpb = tokens_per_block(s->H);
     hipLaunchKernelGGL(k_combine, dim3((unsigned)(((int64_t)s->T + tpb - 1) / tpb)), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(pool_out), slot_to_pool, topk_w,
                        (int64_t)s->T, s->H, s->K, tpb, static_cast<uint16_t*>(y));
@@ -516,8 +531,9 @@ int moe_profile_stop(double* stage_ms, int* ncalls) {
 }
 
 const char* moe_profile_stage_name(int stage) {
-    static const char* names[MOE_PROFILE_STAGES] = {"weight_scales", "route_count", "route_scan", "route_scatter",
-                                                    "dispatch", "gemm_l1", "gemm_l2", "combine"};
+    static const char* names[MOE_PROFILE_STAGES] = {"weight_scales", "dispatch",  "route_scan",
+                                                    "route_scatter", "pool_scales", "gemm_l1",
+                                                    "gemm_l2",       "combine"};
     return stage >= 0 && stage < MOE_PROFILE_STAGES ? names[stage] : "?";
 }
 

@@ -77,10 +77,13 @@ __global__ void k_route_scatter(const int64_t* __restrict__ topk_idx,
                                 int32_t* __restrict__ pool_src,
                                 int32_t* __restrict__ slot_to_pool, float* __restrict__ pool_w,
                                 int32_t* __restrict__ pool_tok);
-__global__ void k_dispatch_fp8(const uint16_t* __restrict__ x, int H, int K,
-                               const int32_t* __restrict__ slot_to_pool,
-                               uint8_t* __restrict__ pool, uint8_t* __restrict__ pool_s,
-                               uint8_t* __restrict__ tok_s);
+__global__ void k_dispatch_fp8(const uint16_t* __restrict__ x, int64_t T, int H, int K, int tpb,
+                               const int32_t* __restrict__ slot_to_pool, uint8_t* __restrict__ pool,
+                               uint8_t* __restrict__ pool_s, uint8_t* __restrict__ tok_s);
+__global__ void k_quantise_count(const uint16_t* __restrict__ x, int64_t T, int H, int tpb,
+                                 uint8_t* __restrict__ x_q, uint8_t* __restrict__ tok_s,
+                                 const int64_t* __restrict__ topk_idx, int64_t TK, int E, int ncount,
+                                 int32_t* __restrict__ seg_hist, int32_t* __restrict__ seg_err);
 __global__ void k_pool_scales(const uint32_t* __restrict__ tok_s, int W,
                               const int32_t* __restrict__ pool_tok,
                               const int32_t* __restrict__ offsets, int E, int64_t cap,
@@ -90,12 +93,12 @@ __global__ void k_scales_kmajor(const uint32_t* __restrict__ S, uint32_t* __rest
 __global__ void k_dispatch_bf16(const uint16_t* __restrict__ x, int H, int K,
                                 const int32_t* __restrict__ slot_to_pool,
                                 uint16_t* __restrict__ pool);
-// Tokens per combine block: as many whole rows as fit 8192 columns (at most
-// kCombineMaxTokens), else one.
-constexpr int kCombineMaxTokens = 32;
-inline int combine_tokens_per_block(int H) {
+// Tokens per dispatch / combine block: as many whole rows as fit 8192
+// columns (at most kMaxBlockTokens), else one.
+constexpr int kMaxBlockTokens = 32;
+inline int tokens_per_block(int H) {
     const int t = 8192 / H;
-    return t < 1 ? 1 : (t > kCombineMaxTokens ? kCombineMaxTokens : t);
+    return t < 1 ? 1 : (t > kMaxBlockTokens ? kMaxBlockTokens : t);
 }
 __global__ void k_combine(const uint16_t* __restrict__ o, const int32_t* __restrict__ slot_to_pool,
                           const float* __restrict__ topk_w, int64_t T, int H, int K, int tpb,

@@ -21,13 +21,13 @@ namespace moe {
 // a1: per-segment expert histogram.  One wave per kSegSlots-slot segment, LDS
 // atomics on a per-wave histogram.  Indices >= E are counted as errors and
 // otherwise treated as masked.
-__global__ __launch_bounds__(kRouteThreads) void k_route_count(
-    const int64_t* __restrict__ topk_idx, int64_t TK, int E, int32_t* __restrict__ seg_hist,
-    int32_t* __restrict__ seg_err) {
-    extern __shared__ int32_t lds_hist[];  // [kRouteWaves][E]
+__device__ __forceinline__ void route_count_block(const int64_t* __restrict__ topk_idx, int64_t TK,
+                                                  int E, int32_t* __restrict__ seg_hist,
+                                                  int32_t* __restrict__ seg_err, int64_t blk,
+                                                  int32_t* lds_hist /* [kRouteWaves][E] */) {
     const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t nseg = (TK + kSegSlots - 1) / kSegSlots;
-    const int64_t seg = (int64_t)blockIdx.x * kRouteWaves + wv;
+    const int64_t seg = blk * kRouteWaves + wv;
     int32_t* h = lds_hist + wv * E;
     for (int e = lane; e < E; e += kWave) h[e] = 0;
     __syncthreads();
@@ -50,6 +50,13 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_count(
         const unsigned long long any_bad = __ballot(bad);
         if (lane == 0) seg_err[seg] = any_bad ? 1 : 0;
     }
+}
+
+__global__ __launch_bounds__(kRouteThreads) void k_route_count(
+    const int64_t* __restrict__ topk_idx, int64_t TK, int E, int32_t* __restrict__ seg_hist,
+    int32_t* __restrict__ seg_err) {
+    extern __shared__ int32_t lds_hist[];  // [kRouteWaves][E]
+    route_count_block(topk_idx, TK, E, seg_hist, seg_err, blockIdx.x, lds_hist);
 }
 
 // a2: exclusive prefix sum.  One block.  The segment histogram [nseg][E] is
@@ -207,53 +214,103 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(
     }
 }
 
-// a4: gather + quantise.  One block per token row.  Each lane owns 8
-// consecutive columns (one 16-byte load), a quad of lanes owns one 32-column
-// scale group: amax over the quad, UE8M0 scale, e4m3 codes, then the 8 code
-// bytes go to every valid pool row of the token -- or, with a null
-// slot_to_pool, once to row t of a token-major copy (the fused layer's L1
-// reads token rows from it directly).  The scale bytes go either to every
-// pool row of the token (pool_s, [rows][H/32]) or once to the token (tok_s,
-// [T][H/128] words holding groups 4w, 4w+2, 4w+1, 4w+3 in byte order, the
-// word form the GEMM loads); a null pointer skips that form.
-__global__ __launch_bounds__(256) void k_dispatch_fp8(const uint16_t* __restrict__ x, int H,
-                                                     int K, const int32_t* __restrict__ slot_to_pool,
+// a4: gather + quantise.  A block takes tpb consecutive token rows (as many
+// as fit 8192 columns, else one) as one flat span; each lane owns 8
+// consecutive columns of up to four 2048-column chunks, whose 16-byte loads
+// all go out first.  A quad of lanes owns one 32-column scale group: amax
+// over the quad, UE8M0 scale, e4m3 codes, then the 8 code bytes go to every
+// valid pool row of the token -- or, with a null slot_to_pool, once to row t
+// of a token-major copy (the fused layer's L1 reads token rows from it
+// directly).  The scale bytes go either to every pool row of the token
+// (pool_s, [rows][H/32]) or once to the token (tok_s, [T][H/128] words
+// holding groups 4w, 4w+2, 4w+1, 4w+3 in byte order, the word form the GEMM
+// loads); a null pointer skips that form.
+__device__ __forceinline__ void dispatch_fp8_block(const uint16_t* __restrict__ x, int64_t T,
+                                                   int H, int K, int tpb,
+                                                   const int32_t* __restrict__ slot_to_pool,
+                                                   uint8_t* __restrict__ pool,
+                                                   uint8_t* __restrict__ pool_s,
+                                                   uint8_t* __restrict__ tok_s, int64_t blk) {
+    __shared__ int32_t rows[kMaxBlockTokens * 64];
+    const int64_t t0 = blk * tpb;
+    if (!slot_to_pool) K = 1;  // token-major only: row t of pool is token t
+    for (int i = threadIdx.x; i < tpb * K; i += 256) {
+        const int64_t t = t0 + i / K;
+        rows[i] = t >= T ? -1 : (slot_to_pool ? slot_to_pool[t0 * K + i] : (int32_t)t);
+    }
+    __syncthreads();
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    // the block's tokens as one flat span; H % 32 == 0, so a quad's 32
+    // columns (one scale group) belong to one token
+    const int span = tpb * H;
+    for (int c00 = threadIdx.x * 8; c00 < span; c00 += 4 * 256 * 8) {
+        int tok[4], col[4];
+        u32x4 v[4];
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+            const int p = c00 + hh * 256 * 8;
+            const int j = p < span ? p / H : -1;
+            tok[hh] = (j >= 0 && t0 + j < T) ? j : -1;
+            col[hh] = j >= 0 ? p - j * H : 0;
+            const u32x4 z = {0, 0, 0, 0};
+            // streamed: each x byte is read once
+            v[hh] = tok[hh] >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                                       x + (t0 + tok[hh]) * H + col[hh]))
+                                 : z;
+        }
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+            float f[8] = {bf16_lo(v[hh].x), bf16_hi(v[hh].x), bf16_lo(v[hh].y), bf16_hi(v[hh].y),
+                          bf16_lo(v[hh].z), bf16_hi(v[hh].z), bf16_lo(v[hh].w), bf16_hi(v[hh].w)};
+            float amax = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+            amax = quad_max(amax);  // all lanes take part (a quad is valid or not as a whole)
+            if (tok[hh] < 0) continue;
+            const uint32_t b = ue8m0_e4m3(amax);
+            uint2 q;
+            q.x = pack_fp8x4(unscale(f[0], b), unscale(f[1], b), unscale(f[2], b), unscale(f[3], b));
+            q.y = pack_fp8x4(unscale(f[4], b), unscale(f[5], b), unscale(f[6], b), unscale(f[7], b));
+            const int64_t t = t0 + tok[hh];
+            const int c0 = col[hh];
+            if (tok_s && (threadIdx.x & 3) == 0) {
+                const int gi = c0 / 32;  // group gi is byte (0, 2, 1, 3)[gi % 4] of word gi / 4
+                tok_s[t * (H / 32) + (gi & ~3) + (((gi & 1) << 1) | ((gi >> 1) & 1))] = (uint8_t)b;
+            }
+            for (int k = 0; k < K; ++k) {
+                const int32_t r = rows[tok[hh] * K + k];
+                if (r < 0) continue;
+                *reinterpret_cast<uint2*>(pool + (int64_t)r * H + c0) = q;
+                if (pool_s && (threadIdx.x & 3) == 0) pool_s[(int64_t)r * (H / 32) + c0 / 32] = (uint8_t)b;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_dispatch_fp8(const uint16_t* __restrict__ x, int64_t T,
+                                                     int H, int K, int tpb,
+                                                     const int32_t* __restrict__ slot_to_pool,
                                                      uint8_t* __restrict__ pool,
                                                      uint8_t* __restrict__ pool_s,
                                                      uint8_t* __restrict__ tok_s) {
-    __shared__ int32_t rows[64];
-    const int64_t t = blockIdx.x;
-    if (!slot_to_pool) {
-        K = 1;
-        if (threadIdx.x == 0) rows[0] = (int32_t)t;
-    } else if (threadIdx.x < K) {
-        rows[threadIdx.x] = slot_to_pool[t * K + threadIdx.x];
-    }
-    __syncthreads();
-    const uint16_t* xr = x + t * H;
-    for (int c0 = threadIdx.x * 8; c0 < H; c0 += 256 * 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xr + c0);
-        float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-        float amax = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
-        amax = quad_max(amax);
-        const uint32_t b = ue8m0_e4m3(amax);
-        uint2 q;
-        q.x = pack_fp8x4(unscale(f[0], b), unscale(f[1], b), unscale(f[2], b), unscale(f[3], b));
-        q.y = pack_fp8x4(unscale(f[4], b), unscale(f[5], b), unscale(f[6], b), unscale(f[7], b));
-        if (tok_s && (threadIdx.x & 3) == 0) {
-            const int gi = c0 / 32;  // group gi is byte (0, 2, 1, 3)[gi % 4] of word gi / 4
-            tok_s[t * (H / 32) + (gi & ~3) + (((gi & 1) << 1) | ((gi >> 1) & 1))] = (uint8_t)b;
-        }
-        for (int k = 0; k < K; ++k) {
-            const int32_t r = rows[k];
-            if (r < 0) continue;
-            *reinterpret_cast<uint2*>(pool + (int64_t)r * H + c0) = q;
-            if (pool_s && (threadIdx.x & 3) == 0) pool_s[(int64_t)r * (H / 32) + c0 / 32] = (uint8_t)b;
-        }
-    }
+    dispatch_fp8_block(x, T, H, K, tpb, slot_to_pool, pool, pool_s, tok_s, blockIdx.x);
+}
+
+// The fused layer's first launch: blocks [0, ncount) compute the a1
+// per-segment histograms, the others quantise the token rows token-major
+// (the two are independent, so the histogram hides behind the row stream).
+__global__ __launch_bounds__(256) void k_quantise_count(const uint16_t* __restrict__ x, int64_t T,
+                                                       int H, int tpb, uint8_t* __restrict__ x_q,
+                                                       uint8_t* __restrict__ tok_s,
+                                                       const int64_t* __restrict__ topk_idx,
+                                                       int64_t TK, int E, int ncount,
+                                                       int32_t* __restrict__ seg_hist,
+                                                       int32_t* __restrict__ seg_err) {
+    extern __shared__ int32_t lds_hist[];  // [kRouteWaves][E]
+    if ((int)blockIdx.x < ncount)
+        route_count_block(topk_idx, TK, E, seg_hist, seg_err, blockIdx.x, lds_hist);
+    else
+        dispatch_fp8_block(x, T, H, 1, tpb, nullptr, x_q, nullptr, tok_s, blockIdx.x - ncount);
 }
 
 // A-scale words of the pool rows in packed k-major order (the layout the L1
@@ -357,8 +414,8 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
                                                 const float* __restrict__ topk_w, int64_t T,
                                                 int H, int K, int tpb,
                                                 uint16_t* __restrict__ y) {
-    __shared__ int32_t rows[kCombineMaxTokens * 64];
-    __shared__ float wts[kCombineMaxTokens * 64];
+    __shared__ int32_t rows[kMaxBlockTokens * 64];
+    __shared__ float wts[kMaxBlockTokens * 64];
     const int64_t t0 = (int64_t)blockIdx.x * tpb;
     for (int i = threadIdx.x; i < tpb * K; i += 256) {
         const int64_t t = t0 + i / K;
