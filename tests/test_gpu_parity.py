@@ -344,3 +344,15 @@ def test_full_size_workload(name):
     ref = oracle.forward_tokens(inp, toks.astype(np.int32))
     worst = check_y(y[toks], ref, inp["topk_idx"][toks])
     say(name, "sampled tokens", len(toks), "max rel l2", worst)
+    # the benchmark times the packed-scale entry: same y, bit for bit
+    import combine_dispatch_amd as moe
+    T, I, E = inp["T"], inp["I"], inp["E"]
+    dev = to_dev(inp)
+    packed = torch.empty(moe.moe_packed_scales_bytes(H, I, E), dtype=torch.uint8, device=DEV)
+    moe.moe_pack_weight_scales(dev["S1"], dev["S2"], packed, E=E, H=H, I=I)
+    yp = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    moe.moe_fused_forward_packed(dev["x"], dev["topk_idx"], dev["topk_w"], dev["W1q"],
+                                 dev["W2q"], packed, yp, ws, E=E, I=I)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_bits(yp), y)
+    say(name, "packed-scale entry bit-identical")
