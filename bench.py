@@ -16,7 +16,9 @@ Prints ONE JSON line (rank 0):
   value        whole-layer TFLOP/s = 6*R*H*I / step time (R = routed rows)
   routed_rows_per_s
   roofline     the dominant kernel (the L1 GEMM): algorithmic FLOP per launch
-               / its average duration from HIP events on its stream, against
+               / its average duration from HIP events on its stream (recorded
+               by the library around each launch over a second run of the
+               same number of steps; the first, timed run has none), against
                the FP8 dense MFMA peak (the FP8 x FP4 scaled MFMA runs at the
                FP8 rate)
   cpu_baseline the CPU oracle on a bounded sample of the same workload
@@ -143,12 +145,10 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` whole-layer steps.  The library records
-    # HIP events around each of its launches on the same stream, so the
-    # per-kernel durations come from this very region.
+    # timed region: exactly `steps` whole-layer steps, nothing else on the
+    # stream between them
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    moe.moe_profile_start(a.steps)
     wall0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(a.steps):
@@ -157,6 +157,19 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = ev0.elapsed_time(ev1) / a.steps
+
+    # per-kernel durations: the same number of steps again, with the library
+    # recording a HIP event on the launch stream around each of its launches.
+    # An event between two launches delays the second by a few microseconds,
+    # so this region's step time is reported separately and not as `value`.
+    ep0, ep1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    moe.moe_profile_start(a.steps)
+    ep0.record(stream)
+    for _ in range(a.steps):
+        step()
+    ep1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step_events = ep0.elapsed_time(ep1) / a.steps
     stage_ms, ncalls = moe.moe_profile_stop()
     per_launch = {k: v / max(ncalls, 1) for k, v in stage_ms.items()}
 
@@ -232,6 +245,7 @@ def main():
                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(l1_tflops / PEAK_TFLOPS, 4),
                      "traffic": traffic},
         "kernels_ms_per_launch": {k: round(v, 4) for k, v in per_launch.items()},
+        "ms_per_step_with_kernel_events": round(ms_per_step_events, 4),
         "kernels": {
             "gemm_l2_tflops": round(l2_tflops, 2),
             "dispatch_gbs": round(disp_bytes / (per_launch["dispatch"] * 1e-3) / 1e9, 1),

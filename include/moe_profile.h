@@ -4,7 +4,10 @@
  * While profiling is on, every moe_fused_forward call records a HIP event on
  * its stream before its first launch and after each of its launches, so the
  * time between two consecutive events is one kernel's duration on the GPU
- * (plus the launch gap).  Nothing is synchronised until moe_profile_stop.
+ * (plus the launch gap).  The events are timing-only (created without the
+ * system-scope fence a default event performs when it is recorded, which
+ * would add a gap of several microseconds before each launch).  Nothing is
+ * synchronised until moe_profile_stop, which waits for the whole device.
  * Calls beyond max_calls are not recorded.  Not thread-safe: profile one
  * caller at a time.
  */
