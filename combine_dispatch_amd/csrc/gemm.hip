@@ -46,7 +46,10 @@ namespace {
 
 constexpr int kL1 = 0;
 constexpr int kL2 = 1;
-constexpr int kGroupM = 4;  // m-tiles per tile-order group
+// m-tiles per tile-order group.  Measured on the prefill workload (A/B on one
+// box): 1, 2 and 3 give the same L1 time and an L2 GEMM 1.5-2 % faster than
+// 4; 8 is 3 % slower.
+constexpr int kGroupM = 1;
 
 // Which expert-matrix row (output column) holds LDS B row `nrow` of tile nt.
 // LDS B row n is column c = n%32 of MFMA column tile j = n/32.  The order is
@@ -198,7 +201,7 @@ __device__ __forceinline__ int late_copy(int v) {
 // of 8 and the hardware places workgroup b on XCD b % 8; XCD x owns the
 // logical tiles [total*x/8, total*(x+1)/8) and its workgroups take them
 // round-robin, so the ~32 workgroups of an XCD work on consecutive tiles of
-// one group and share both operands through that XCD's L2.  The stream of K
+// one group and share operands through that XCD's L2.  The stream of K
 // steps runs on across tiles: the last three steps of a tile issue the first
 // loads of the next one at the steady rate, so they land while the epilogue
 // runs.  (The host sizes the grid so that no workgroup has more than
@@ -216,8 +219,10 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     const int Kdim = g.Kdim;
     const int nk = Kdim / kBK;
 
-    // Tile order: groups of kGroupM m-tiles x all n-tiles, m fastest, so the
-    // ~32 workgroups of an XCD cover 4 m-tiles x 8 n-tiles at a time.
+    // Tile order: groups of kGroupM m-tiles x all n-tiles, m fastest; with
+    // one m-tile per group the ~32 workgroups of an XCD cover all n-tiles of
+    // one or two m-tiles at a time (sharing those A rows through its L2)
+    // while the expert's B n-tiles come round again for the next m-tile.
     const int num_m = *g.num_mtiles;
     const int total = num_m * g.ntiles;
     const int xcd = blockIdx.x & 7, nj = (int)gridDim.x >> 3;
