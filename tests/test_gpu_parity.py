@@ -101,17 +101,41 @@ SMALL = [
     dict(T=200, H=256, I=128, E=1000, K=8, routing="zipf", seed=45, mask_p=0.02),
     # an expert count that is not a power of two (two scan threads per expert)
     dict(T=150, H=512, I=256, E=257, K=6, routing="uniform", seed=46),
+    # the same expert twice in a token (each slot is its own route)
+    dict(T=120, H=256, I=128, E=8, K=4, routing="uniform", seed=47, dup=True),
+    # the largest top-k
+    dict(T=40, H=256, I=128, E=96, K=64, routing="uniform", seed=48),
+    # one token
+    dict(T=1, H=512, I=256, E=4, K=2, routing="uniform", seed=49),
+    # experts with 32, 33, 64, 65, 256 and 257 rows: narrow tiles with one
+    # and two row tiles, the first full-mode short tile, one whole tile and
+    # one row past it
+    dict(T=707, H=256, I=128, E=6, K=1, routing="uniform", seed=50,
+         counts=(32, 33, 64, 65, 256, 257)),
 ]
+SMALL_IDS = ["tiny", "ragged", "dense", "sparse", "masked", "e1000", "e257", "dup", "k64", "t1",
+             "tile_edges"]
 
 
 def small_inputs(case):
     if "name" in case:
         return moe_inputs.config_inputs(case["name"])
-    return moe_inputs.make_inputs(**case)
+    kw = {k: v for k, v in case.items() if k not in ("dup", "counts")}
+    inp = moe_inputs.make_inputs(**kw)
+    rng = np.random.default_rng(case["seed"])
+    idx = inp["topk_idx"]
+    if case.get("dup"):
+        # every third token repeats its first expert in slot 1
+        idx[::3, 1] = idx[::3, 0]
+    if "counts" in case:
+        # token t goes to the expert given by a seeded shuffle of the counts
+        assert case["K"] == 1 and sum(case["counts"]) == case["T"]
+        e = np.repeat(np.arange(len(case["counts"]), dtype=np.int64), case["counts"])
+        idx[:, 0] = rng.permutation(e)
+    return inp
 
 
-@pytest.mark.parametrize("case", SMALL, ids=["tiny", "ragged", "dense", "sparse", "masked",
-                                             "e1000", "e257"])
+@pytest.mark.parametrize("case", SMALL, ids=SMALL_IDS)
 def test_forward_matches_oracle_small(case):
     inp = small_inputs(case)
     say("case", case)
