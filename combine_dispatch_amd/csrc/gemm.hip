@@ -654,8 +654,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
                         b[rr] = ue8m0_e4m3_bits(m[rr]);
-                        codes[rr] = pack_fp8x4(unscale(a[rr][0], b[rr]), unscale(a[rr][1], b[rr]),
-                                               unscale(a[rr][2], b[rr]), unscale(a[rr][3], b[rr]));
+                        codes[rr] = pack_fp8x4_scaled(a[rr][0], a[rr][1], a[rr][2], a[rr][3], b[rr]);
                     }
                     // the byte of row rsel (lanes rsel < 4 store it): one shift of
                     // the four bytes packed in a word instead of a select chain
@@ -745,7 +744,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
                         b[rr] = ue8m0_e4m3_bits(m[rr]);
-                        const uint32_t code = pack_fp8x2(unscale(a[rr], b[rr]), 0.f);
+                        const uint32_t code = pack_fp8x2_scaled(a[rr], 0.f, b[rr]);
                         __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, q_rs, (lrow0 + rr) * I + l32, 0, kStoreNT);
                     }
                     // lanes l32 = 0..3 store the scale byte of rows lrow0 + l32

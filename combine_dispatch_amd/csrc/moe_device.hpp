@@ -32,18 +32,6 @@ __device__ __forceinline__ float round_bf16(float v) {
     return __uint_as_float(pack_bf16x2(v, 0.f) << 16);
 }
 
-// Two fp32 -> two e4m3 bytes in the low half (v_cvt_pk_fp8_f32, OCP e4m3fn,
-// round to nearest even).
-__device__ __forceinline__ uint32_t pack_fp8x2(float a, float b) {
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
-}
-
-// Four fp32 -> four e4m3 bytes.
-__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
-}
-
 // UE8M0 scale byte for an e4m3 group: the smallest b with
 // amax <= 448 * 2^(b-127), from the fp32 fields of amax: exponent field
 // minus 8, plus one when the significand exceeds 1.75 (448 = 1.75 * 2^8).
@@ -69,9 +57,24 @@ __device__ __forceinline__ uint32_t swap_bytes12(uint32_t v) {
     return (v & 0xFF0000FFu) | ((v >> 8) & 0x0000FF00u) | ((v << 8) & 0x00FF0000u);
 }
 
-// v * 2^(127-b): exact (v_ldexp_f32).
-__device__ __forceinline__ float unscale(float v, uint32_t b) {
-    return __builtin_amdgcn_ldexpf(v, 127 - (int)b);
+// e4m3 bytes of v * 2^(127-s) for a UE8M0 scale byte s, the scaling done by
+// the conversion itself (v_cvt_scalef32_pk_fp8_f32 divides by its scale
+// operand; an fp32 whose exponent field is s is 2^(s-127), s = 0 included).
+// Measured on gfx950: the same bytes as v_ldexp_f32 by 127-s followed by
+// v_cvt_pk_fp8_f32, on 2^21 pairs of exact codes, ties, e4m3 subnormals and
+// other values, over scale bytes 0..254.
+typedef short short2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_fp8x2_scaled(float a, float b, uint32_t s) {
+    const short2_t z = {0, 0};
+    const short2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a, b, __uint_as_float(s << 23), false);
+    return (uint32_t)(uint16_t)r.x;
+}
+__device__ __forceinline__ uint32_t pack_fp8x4_scaled(float a, float b, float c, float d, uint32_t s) {
+    const float sc = __uint_as_float(s << 23);
+    const short2_t z = {0, 0};
+    const short2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a, b, sc, false);
+    const short2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, c, d, sc, true);
+    return (uint32_t)(uint16_t)r.x | ((uint32_t)(uint16_t)r.y << 16);
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

@@ -269,8 +269,8 @@ __device__ __forceinline__ void dispatch_fp8_block(const uint16_t* __restrict__ 
             if (tok[hh] < 0) continue;
             const uint32_t b = ue8m0_e4m3(amax);
             uint2 q;
-            q.x = pack_fp8x4(unscale(f[0], b), unscale(f[1], b), unscale(f[2], b), unscale(f[3], b));
-            q.y = pack_fp8x4(unscale(f[4], b), unscale(f[5], b), unscale(f[6], b), unscale(f[7], b));
+            q.x = pack_fp8x4_scaled(f[0], f[1], f[2], f[3], b);
+            q.y = pack_fp8x4_scaled(f[4], f[5], f[6], f[7], b);
             const int64_t t = t0 + tok[hh];
             const int c0 = col[hh];
             if (tok_s && (threadIdx.x & 3) == 0) {
