@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--scales", choices=("packed", "canonical"), default="packed",
                    help="packed: weight scales laid out once before timing (default); "
                         "canonical: moe_fused_forward re-lays them every step")
+    p.add_argument("--graph", action="store_true",
+                   help="also capture one moe_fused_forward_packed step into a HIP graph and report the replayed step "
+                        "time (ms_per_step_graph) beside the main number")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="after the timed region, run one plain device-to-device copy of this "
                         "many MiB (the known-size kernel that scales the HBM byte counters)")
@@ -195,6 +198,35 @@ def main():
     cold_ms = ec0.elapsed_time(ec1)
     del scrub
 
+    graph_ms = None
+    if a.graph:
+        # one step captured into a HIP graph (the library allocates, sets and
+        # synchronises nothing, and takes every size from the device), then
+        # the same number of replays timed
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            moe.moe_fused_forward_packed(d["x"], d["topk_idx"], d["topk_w"], d["W1q"], d["W2q"],
+                                         packed, y, ws, E=E, I=I, stream=cap)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            moe.moe_fused_forward_packed(d["x"], d["topk_idx"], d["topk_w"], d["W1q"], d["W2q"],
+                                         packed, y, ws, E=E, I=I,
+                                         stream=torch.cuda.current_stream())
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        eg0, eg1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        eg0.record(stream)
+        for _ in range(a.steps):
+            graph.replay()
+        eg1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = eg0.elapsed_time(eg1) / a.steps
+        del graph
+
     if a.copy_mib > 0:
         n = a.copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -256,6 +288,7 @@ def main():
         ("ms_per_step_canonical_scales" if a.scales == "packed"
          else "ms_per_step_packed_scales"): round(other_ms, 4),
         "cold_ms_per_step": round(cold_ms, 4),
+        **({"ms_per_step_graph": round(graph_ms, 4)} if graph_ms is not None else {}),
         "wall_s_timed": round(wall, 4),
         "input_gen_s": round(gen_s, 2),
     }
