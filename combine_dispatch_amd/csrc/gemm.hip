@@ -47,7 +47,7 @@ namespace {
 constexpr int kL1 = 0;
 constexpr int kL2 = 1;
 // m-tiles per tile-order group.  Measured on the prefill workload (A/B on one
-// box): 1, 2 and 3 give the same L1 time and an L2 GEMM 1.5-2 % faster than
+// machine): 1, 2 and 3 give the same L1 time and an L2 GEMM 1.5-2 % faster than
 // 4; 8 is 3 % slower.
 constexpr int kGroupM = 1;
 
