@@ -76,8 +76,18 @@ def _gen():
         L.gen_normal_f32.argtypes = [u64, u32, ctypes.c_double, ctypes.c_double, vp, i64]
         L.gen_normal_bf16.argtypes = [u64, u32, vp, i64]
         L.gen_fp4_weights.argtypes = [u64, u32, ctypes.c_double, i64, ctypes.c_int32, vp, vp]
+        L.gen_philox4x32_10.argtypes = [vp, vp, vp]
         _lib = L
     return _lib
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    """One block of the generator: four uint32 words from counter ctr[4], key key[2]."""
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.empty(4, np.uint32)
+    _gen().gen_philox4x32_10(c.ctypes.data, k.ctypes.data, out.ctypes.data)
+    return out
 
 
 def normal_f32(seed: int, stream: int, n: int, mean=0.0, std=1.0) -> np.ndarray:

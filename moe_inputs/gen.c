@@ -52,6 +52,13 @@ static u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
     return c;
 }
 
+/* One Philox4x32-10 block: out = philox(ctr, key), for known-answer checks. */
+void gen_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    u32x4 c = {{ctr[0], ctr[1], ctr[2], ctr[3]}};
+    const u32x4 r = philox4x32_10(c, key[0], key[1]);
+    memcpy(out, r.v, sizeof r.v);
+}
+
 /* Four N(0,1) doubles from counter block `blk` of stream `stream`. */
 static void normals4(uint64_t seed, uint32_t stream, uint64_t blk, double out[4]) {
     u32x4 c = {{(uint32_t)blk, (uint32_t)(blk >> 32), stream, 0u}};
