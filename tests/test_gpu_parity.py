@@ -169,11 +169,21 @@ def test_forward_is_deterministic():
 # ----------------------------------------------------------------------------
 # dispatch and combine entry points on their own
 # ----------------------------------------------------------------------------
+# blocks of 23 tokens (H = 352) and of 4 (H = 2048), one token over several
+# chunks (H = 7168), the largest top-k, one token
+DISPATCH_CASES = [dict(T=513, H=352, E=13, K=5, routing="zipf", mask_p=0.1),
+                  dict(T=300, H=2048, E=16, K=8, routing="uniform"),
+                  dict(T=40, H=7168, E=32, K=8, routing="uniform"),
+                  dict(T=9, H=256, E=96, K=64, routing="uniform"),
+                  dict(T=1, H=512, E=4, K=2, routing="uniform")]
+
+
+@pytest.mark.parametrize("case", DISPATCH_CASES,
+                         ids=["h352", "h2048", "h7168", "k64", "t1"])
 @pytest.mark.parametrize("payload", [0, 1], ids=["fp8", "bf16"])
-def test_dispatch_entry_matches_oracle(payload):
+def test_dispatch_entry_matches_oracle(payload, case):
     import combine_dispatch_amd as moe
-    inp = moe_inputs.make_inputs(T=513, H=352, I=32, E=13, K=5, routing="zipf", seed=51,
-                                 mask_p=0.1, weights=False)
+    inp = moe_inputs.make_inputs(I=32, seed=51, weights=False, **case)
     T, H, E, K = inp["T"], inp["H"], inp["E"], inp["K"]
     ref = oracle.dispatch(inp["x"], inp["topk_idx"], inp["topk_w"], E, payload)
     dev = to_dev(inp)
