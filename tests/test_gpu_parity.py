@@ -211,6 +211,37 @@ def test_dispatch_entry_matches_oracle(payload, case):
         np.testing.assert_array_equal(scales.cpu().numpy()[:R], ref["pool_scales"][:R])
 
 
+@pytest.mark.parametrize("name", ["tiny", "small", "prefill", "skewed", "many"])
+def test_dispatch_entry_on_workloads(name):
+    """moe_dispatch (FP8 payload) on the five workloads at full size: routing
+    arrays, pool codes and pool scale bytes bit-exact against the oracle."""
+    import combine_dispatch_amd as moe
+    say("dispatch", name)
+    inp = moe_inputs.config_inputs(name)
+    T, H, E, K = inp["T"], inp["H"], inp["E"], inp["K"]
+    ref = oracle.dispatch(inp["x"], inp["topk_idx"], inp["topk_w"], E, 0)
+    dev = to_dev({k: inp[k] for k in ("x", "topk_idx", "topk_w")})
+    i32 = dict(dtype=torch.int32, device=DEV)
+    counts, offsets = torch.empty(E, **i32), torch.empty(E + 1, **i32)
+    pool_src, s2p = torch.empty(T * K, **i32), torch.empty(T * K, **i32)
+    pool_w = torch.empty(T * K, dtype=torch.float32, device=DEV)
+    pool = torch.empty((T * K, H), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((T * K, H // 32), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(moe.moe_dispatch_workspace_bytes(T, H, E, K), dtype=torch.uint8, device=DEV)
+    moe.moe_dispatch(dev["x"], dev["topk_idx"], dev["topk_w"], E, 0, counts, offsets, pool_src,
+                     s2p, pool_w, pool, scales, ws)
+    torch.cuda.synchronize()
+    R = int(ref["offsets"][-1])
+    np.testing.assert_array_equal(counts.cpu().numpy(), ref["counts"])
+    np.testing.assert_array_equal(offsets.cpu().numpy(), ref["offsets"])
+    np.testing.assert_array_equal(pool_src.cpu().numpy()[:R], ref["pool_src"][:R])
+    np.testing.assert_array_equal(s2p.cpu().numpy(), ref["slot_to_pool"])
+    np.testing.assert_array_equal(pool_w.cpu().numpy()[:R], ref["pool_w"][:R])
+    np.testing.assert_array_equal(pool.cpu().numpy()[:R], ref["pool"][:R])
+    np.testing.assert_array_equal(scales.cpu().numpy()[:R], ref["pool_scales"][:R])
+    say(name, "dispatch bit-exact, R =", R)
+
+
 # (T, H, K): blocks of 8, 4, 2, 1 and 32 tokens with a ragged last block, a
 # partly used chunk (H = 3072), and a row longer than one pass (H = 16384).
 COMBINE_SHAPES = [(777, 1024, 8), (1001, 2048, 8), (333, 3072, 6), (65, 7168, 8), (130, 40, 64),
