@@ -76,7 +76,7 @@ def lib():
         L.oracle_forward.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp,
                                      ctypes.POINTER(_Mid)]
         L.oracle_forward_tokens.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp,
-                                            i32, vp, vp]
+                                            i32, vp, vp, vp, vp]
         L.oracle_num_threads.restype = i32
         _lib = L
     return _lib
@@ -217,15 +217,21 @@ def forward(inp: dict, intermediates: bool = False):
     return y
 
 
-def forward_tokens(inp: dict, tokens) -> np.ndarray:
-    """Brute-force per-token forward for the listed token indices -> bf16 rows."""
+def forward_tokens(inp: dict, tokens, activations: bool = False):
+    """Brute-force per-token forward for the listed token indices -> bf16 rows;
+    with ``activations``, also each slot's requantised activation row:
+    (y, act_q [n][K][I], act_s [n][K][I/32]), zero for masked slots."""
     T, H, I, E, K = (inp[k] for k in ("T", "H", "I", "E", "K"))
     s = Shape(T, H, I, E, K)
     tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
     y = np.zeros((tok.size, H), np.uint16)
+    aq = np.zeros((tok.size, K, I), np.uint8) if activations else None
+    as_ = np.zeros((tok.size, K, I // 32), np.uint8) if activations else None
     args = [np.ascontiguousarray(inp[k]) for k in ("x", "topk_idx", "topk_w", "W1q", "S1", "W2q", "S2")]
     _check(lib().oracle_forward_tokens(ctypes.byref(s), *[_p(a) for a in args], tok.size, _p(tok),
-                                       _p(y)), "forward_tokens")
+                                       _p(y), _p(aq), _p(as_)), "forward_tokens")
+    if activations:
+        return y, aq, as_
     return y
 
 

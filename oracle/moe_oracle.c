@@ -426,7 +426,7 @@ int oracle_forward_tokens(const oracle_shape_t* s, const uint16_t* x,
                           const int64_t* topk_idx, const float* topk_w,
                           const uint8_t* W1q, const uint8_t* S1, const uint8_t* W2q,
                           const uint8_t* S2, int n_tokens, const int32_t* tokens,
-                          uint16_t* y_rows) {
+                          uint16_t* y_rows, uint8_t* aq_slots, uint8_t* as_slots) {
     if (!shape_ok(s) || n_tokens < 0) return -1;
     const int T = s->T, H = s->H, E = s->E, K = s->K;
     float* xrow = (float*)malloc((size_t)H * sizeof(float));
@@ -452,8 +452,10 @@ int oracle_forward_tokens(const oracle_shape_t* s, const uint16_t* x,
                 break;
             }
             if (e < 0) continue;
+            const int64_t slot = (int64_t)i * K + k;
             rc = expert_row(s, (int)e, xq, xs, topk_w[(int64_t)t * K + k], W1q, S1, W2q, S2, orow,
-                            NULL, NULL, NULL, 1);
+                            NULL, aq_slots ? aq_slots + slot * s->I : NULL,
+                            as_slots ? as_slots + slot * (s->I / 32) : NULL, 1);
             if (rc) break;
             for (int h = 0; h < H; ++h) acc[h] = acc[h] + oracle_bf16_to_f32(orow[h]);
         }

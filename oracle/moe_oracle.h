@@ -102,12 +102,15 @@ int oracle_forward(const oracle_shape_t* s, const uint16_t* x, const int64_t* to
 
 /* ---- the same layer, brute force: for each listed token, each valid slot
  * runs quantise -> L1 -> SwiGLU -> requant -> L2 on that one row, then the
- * slots are summed.  y_rows is [n_tokens][H]. */
+ * slots are summed.  y_rows is [n_tokens][H].  aq_slots ([n_tokens][K][I]
+ * e4m3 codes) and as_slots ([n_tokens][K][I/32] scale bytes), when not NULL,
+ * receive each valid slot's requantised activation row (masked slots are left
+ * as they are). */
 int oracle_forward_tokens(const oracle_shape_t* s, const uint16_t* x,
                           const int64_t* topk_idx, const float* topk_w,
                           const uint8_t* W1q, const uint8_t* S1, const uint8_t* W2q,
                           const uint8_t* S2, int n_tokens, const int32_t* tokens,
-                          uint16_t* y_rows);
+                          uint16_t* y_rows, uint8_t* aq_slots, uint8_t* as_slots);
 
 /* Threads the parallel loops use (OpenMP). */
 int oracle_num_threads(void);

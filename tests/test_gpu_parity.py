@@ -406,9 +406,15 @@ def test_full_size_workload(name):
     # y on sampled tokens (including any fully masked one) against brute force
     masked = np.nonzero((inp["topk_idx"] < 0).all(axis=1))[0][:2]
     toks = np.unique(np.concatenate([rng.integers(0, inp["T"], 6), [0, inp["T"] - 1], masked]))
-    ref = oracle.forward_tokens(inp, toks.astype(np.int32))
+    ref, aq, as_ = oracle.forward_tokens(inp, toks.astype(np.int32), activations=True)
     worst = check_y(y[toks], ref, inp["topk_idx"][toks])
     say(name, "sampled tokens", len(toks), "max rel l2", worst)
+    # the L1 epilogue's e4m3 activations of those tokens' routes, at their pool rows
+    s2p = view(ws, inp, "slot_to_pool").reshape(inp["T"], K)[toks]
+    valid = s2p >= 0
+    check_act(view(ws, inp, "act_q", R)[s2p[valid]], view(ws, inp, "act_s", R)[s2p[valid]],
+              aq[valid], as_[valid])
+    say(name, "sampled routes' activations within the FP8 rule:", int(valid.sum()))
     # the benchmark times the packed-scale entry: same y, bit for bit
     import combine_dispatch_amd as moe
     T, I, E = inp["T"], inp["I"], inp["E"]

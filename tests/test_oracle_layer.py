@@ -214,10 +214,16 @@ def test_grouped_equals_per_token_brute_force():
     for inp in (moe_inputs.config_inputs("tiny"),
                 moe_inputs.make_inputs(T=37, H=96, I=64, E=6, K=4, routing="zipf", seed=21,
                                        mask_p=0.3)):
-        y = oracle.forward(inp)
+        y, mid = oracle.forward(inp, intermediates=True)
         toks = np.arange(inp["T"], dtype=np.int32)
-        yb = oracle.forward_tokens(inp, toks)
+        yb, aq, as_ = oracle.forward_tokens(inp, toks, activations=True)
         np.testing.assert_array_equal(y, yb)
+        # each slot's activation row equals the grouped path's at its pool row
+        s2p = mid["slot_to_pool"].reshape(inp["T"], inp["K"])
+        valid = s2p >= 0
+        np.testing.assert_array_equal(aq[valid], mid["act_q"][s2p[valid]])
+        np.testing.assert_array_equal(as_[valid], mid["act_s"][s2p[valid]])
+        assert (aq[~valid] == 0).all()
 
 
 def test_worked_example_two_experts_weighted_sum():
