@@ -77,6 +77,9 @@ def lib():
                                      ctypes.POINTER(_Mid)]
         L.oracle_forward_tokens.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp,
                                             i32, vp, vp, vp, vp]
+        L.oracle_l1_act_rows.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, i32, vp, vp, vp, vp,
+                                         vp, vp]
+        L.oracle_l2_rows.argtypes = [ctypes.POINTER(Shape), vp, vp, i32, vp, vp, vp, vp]
         L.oracle_num_threads.restype = i32
         _lib = L
     return _lib
@@ -233,6 +236,44 @@ def forward_tokens(inp: dict, tokens, activations: bool = False):
     if activations:
         return y, aq, as_
     return y
+
+
+def l1_act_rows(inp: dict, experts, tokens, weights, h1: bool = False):
+    """Chosen routed rows through quantise -> L1 -> SwiGLU*w -> requant:
+    row i is token tokens[i] through expert experts[i] with weight weights[i].
+    -> (act_q [n][I], act_s [n][I/32]) or, with ``h1``, (h1 [n][2I] bf16,
+    act_q, act_s)."""
+    T, H, I, E, K = (inp[k] for k in ("T", "H", "I", "E", "K"))
+    s = Shape(T, H, I, E, K)
+    ex = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
+    tk = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    wt = np.ascontiguousarray(np.asarray(weights, dtype=np.float32))
+    n = ex.size
+    assert tk.size == n and wt.size == n
+    aq = np.zeros((n, I), np.uint8)
+    as_ = np.zeros((n, I // 32), np.uint8)
+    h1_rows = np.zeros((n, 2 * I), np.uint16) if h1 else None
+    x, W1q, S1 = (np.ascontiguousarray(inp[k]) for k in ("x", "W1q", "S1"))
+    _check(lib().oracle_l1_act_rows(ctypes.byref(s), _p(x), _p(W1q), _p(S1), n, _p(ex), _p(tk),
+                                    _p(wt), _p(h1_rows), _p(aq), _p(as_)), "l1_act_rows")
+    return (h1_rows, aq, as_) if h1 else (aq, as_)
+
+
+def l2_rows(inp: dict, experts, act_q: np.ndarray, act_s: np.ndarray) -> np.ndarray:
+    """L2 alone on given activation rows (codes [n][I], scale bytes [n][I/32])
+    through experts[i] -> bf16 bits [n][H]."""
+    T, H, I, E, K = (inp[k] for k in ("T", "H", "I", "E", "K"))
+    s = Shape(T, H, I, E, K)
+    ex = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
+    aq = np.ascontiguousarray(act_q, dtype=np.uint8)
+    as_ = np.ascontiguousarray(act_s, dtype=np.uint8)
+    n = ex.size
+    assert aq.shape == (n, I) and as_.shape == (n, I // 32)
+    o = np.zeros((n, H), np.uint16)
+    W2q, S2 = (np.ascontiguousarray(inp[k]) for k in ("W2q", "S2"))
+    _check(lib().oracle_l2_rows(ctypes.byref(s), _p(W2q), _p(S2), n, _p(ex), _p(aq), _p(as_),
+                                _p(o)), "l2_rows")
+    return o
 
 
 def num_threads() -> int:

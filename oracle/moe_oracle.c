@@ -288,6 +288,30 @@ static uint16_t dot_bf16(const double* a_deq, const uint8_t* Wq, const uint8_t* 
     return oracle_f32_to_bf16((float)acc);
 }
 
+/* The same dot product with the weight row's scale looked up once per group
+ * of 32 along k instead of once per element: every weight value, product
+ * and partial sum is the same double as in dot_bf16 (e2m1 value times a
+ * power of two is exact either way; the sum runs in the same ascending k
+ * order), so the results are identical.  Used for the single-row entries. */
+static uint16_t dot_bf16_grouped(const double* a_deq, const uint8_t* Wq, const uint8_t* S,
+                                 int Kdim, int64_t n) {
+    const uint8_t* wrow = Wq + n * (Kdim / 2);
+    const uint8_t* srow = S + n * (Kdim / 32);
+    double acc = 0.0;
+    double val[16]; /* value of each e2m1 code under this group's scale */
+    for (int g = 0; g < Kdim / 32; ++g) {
+        const double sc = oracle_ue8m0_value(srow[g]);
+        for (int c = 0; c < 16; ++c) val[c] = (double)oracle_e2m1_to_f32((uint8_t)c) * sc;
+        for (int j = 0; j < 16; ++j) {
+            const int k = 32 * g + 2 * j; /* byte j holds k (low nibble) and k + 1 */
+            const uint8_t byte = wrow[k / 2];
+            acc += a_deq[k] * val[byte & 0xF];
+            acc += a_deq[k + 1] * val[byte >> 4];
+        }
+    }
+    return oracle_f32_to_bf16((float)acc);
+}
+
 /* a6: SwiGLU scaled by the routing weight, fp32 throughout, in the pages'
  * order: e = exp(-g), d = 1 + e, s = g / d, a = (s * u) * w.  [P1] SwiGLU
  * snippet; [P3] section 4.2 (weight applied in the L1 epilogue). */
@@ -301,6 +325,60 @@ static float swiglu_w(uint16_t gate_bf16, uint16_t up_bf16, float w) {
     return su * w;
 }
 
+/* L1 (a5), SwiGLU*w (a6) and requant (a7) of one routed row.  xq/xs: the
+ * row's e4m3 codes and scales; w: its routing weight.  Writes the row's e4m3
+ * activation codes aq[I] and scale bytes as[I/32]; h1_row[2I] (the bf16
+ * gate|up) when not NULL.  par != 0 parallelises the output-column loop. */
+static int l1_act_row(const oracle_shape_t* s, int e, const uint8_t* xq, const uint8_t* xs,
+                      float w, const uint8_t* W1q, const uint8_t* S1, uint16_t* h1_row,
+                      uint8_t* aq, uint8_t* as, int par, int grouped) {
+    const int H = s->H, I = s->I;
+    double* xd = (double*)malloc((size_t)H * sizeof(double));
+    uint16_t* h1 = (uint16_t*)malloc((size_t)2 * I * sizeof(uint16_t));
+    float* act = (float*)malloc((size_t)I * sizeof(float));
+    if (!xd || !h1 || !act) {
+        free(xd); free(h1); free(act);
+        return -3;
+    }
+    const uint8_t* W1e = W1q + (int64_t)e * 2 * I * (H / 2);
+    const uint8_t* S1e = S1 + (int64_t)e * 2 * I * (H / 32);
+
+    /* dequantise the activation row (e4m3 code times its group scale) */
+    for (int h = 0; h < H; ++h)
+        xd[h] = (double)oracle_e4m3_to_f32(xq[h]) * oracle_ue8m0_value(xs[h / 32]);
+
+    /* a5: L1, N = 2I columns: [0, I) gate, [I, 2I) up */
+#pragma omp parallel for schedule(static) if (par)
+    for (int n = 0; n < 2 * I; ++n)
+        h1[n] = grouped ? dot_bf16_grouped(xd, W1e, S1e, H, n) : dot_bf16(xd, W1e, S1e, H, n);
+
+    /* a6 + a7: SwiGLU * w, then e4m3 requant per 32 along I */
+    for (int j = 0; j < I; ++j) act[j] = swiglu_w(h1[j], h1[I + j], w);
+    oracle_quant_e4m3_row(act, I, aq, as);
+
+    if (h1_row) memcpy(h1_row, h1, (size_t)2 * I * sizeof(uint16_t));
+    free(xd); free(h1); free(act);
+    return 0;
+}
+
+/* L2 (a8) of one activation row: K = I, N = H, unweighted, bf16 out.
+ * aq/as: the row's e4m3 codes and scale bytes; writes o_row[H]. */
+static int l2_row(const oracle_shape_t* s, int e, const uint8_t* aq, const uint8_t* as,
+                  const uint8_t* W2q, const uint8_t* S2, uint16_t* o_row, int par, int grouped) {
+    const int H = s->H, I = s->I;
+    double* ad = (double*)malloc((size_t)I * sizeof(double));
+    if (!ad) return -3;
+    const uint8_t* W2e = W2q + (int64_t)e * H * (I / 2);
+    const uint8_t* S2e = S2 + (int64_t)e * H * (I / 32);
+    for (int i = 0; i < I; ++i)
+        ad[i] = (double)oracle_e4m3_to_f32(aq[i]) * oracle_ue8m0_value(as[i / 32]);
+#pragma omp parallel for schedule(static) if (par)
+    for (int h = 0; h < H; ++h)
+        o_row[h] = grouped ? dot_bf16_grouped(ad, W2e, S2e, I, h) : dot_bf16(ad, W2e, S2e, I, h);
+    free(ad);
+    return 0;
+}
+
 /* One routed row through the expert: L1 (a5), SwiGLU*w (a6), requant (a7),
  * L2 (a8).  xq/xs: the row's e4m3 codes and scales.  Writes the bf16 L2
  * row o_row[H]; optional h1_row[2I], aq_row[I], as_row[I/32].
@@ -309,45 +387,18 @@ static int expert_row(const oracle_shape_t* s, int e, const uint8_t* xq, const u
                       float w, const uint8_t* W1q, const uint8_t* S1, const uint8_t* W2q,
                       const uint8_t* S2, uint16_t* o_row, uint16_t* h1_row, uint8_t* aq_row,
                       uint8_t* as_row, int par) {
-    const int H = s->H, I = s->I;
-    double* xd = (double*)malloc((size_t)H * sizeof(double));
-    uint16_t* h1 = (uint16_t*)malloc((size_t)2 * I * sizeof(uint16_t));
-    float* act = (float*)malloc((size_t)I * sizeof(float));
+    const int I = s->I;
     uint8_t* aq = (uint8_t*)malloc((size_t)I);
     uint8_t* as = (uint8_t*)malloc((size_t)I / 32);
-    double* ad = (double*)malloc((size_t)I * sizeof(double));
-    if (!xd || !h1 || !act || !aq || !as || !ad) {
-        free(xd); free(h1); free(act); free(aq); free(as); free(ad);
-        return -3;
+    int rc = -3;
+    if (aq && as) {
+        rc = l1_act_row(s, e, xq, xs, w, W1q, S1, h1_row, aq, as, par, 0);
+        if (rc == 0) rc = l2_row(s, e, aq, as, W2q, S2, o_row, par, 0);
+        if (rc == 0 && aq_row) memcpy(aq_row, aq, (size_t)I);
+        if (rc == 0 && as_row) memcpy(as_row, as, (size_t)I / 32);
     }
-    const uint8_t* W1e = W1q + (int64_t)e * 2 * I * (H / 2);
-    const uint8_t* S1e = S1 + (int64_t)e * 2 * I * (H / 32);
-    const uint8_t* W2e = W2q + (int64_t)e * H * (I / 2);
-    const uint8_t* S2e = S2 + (int64_t)e * H * (I / 32);
-
-    /* dequantise the activation row (e4m3 code times its group scale) */
-    for (int h = 0; h < H; ++h)
-        xd[h] = (double)oracle_e4m3_to_f32(xq[h]) * oracle_ue8m0_value(xs[h / 32]);
-
-    /* a5: L1, N = 2I columns: [0, I) gate, [I, 2I) up */
-#pragma omp parallel for schedule(static) if (par)
-    for (int n = 0; n < 2 * I; ++n) h1[n] = dot_bf16(xd, W1e, S1e, H, n);
-
-    /* a6 + a7: SwiGLU * w, then e4m3 requant per 32 along I */
-    for (int j = 0; j < I; ++j) act[j] = swiglu_w(h1[j], h1[I + j], w);
-    oracle_quant_e4m3_row(act, I, aq, as);
-
-    /* a8: L2, K = I, N = H, unweighted, bf16 out */
-    for (int i = 0; i < I; ++i)
-        ad[i] = (double)oracle_e4m3_to_f32(aq[i]) * oracle_ue8m0_value(as[i / 32]);
-#pragma omp parallel for schedule(static) if (par)
-    for (int h = 0; h < H; ++h) o_row[h] = dot_bf16(ad, W2e, S2e, I, h);
-
-    if (h1_row) memcpy(h1_row, h1, (size_t)2 * I * sizeof(uint16_t));
-    if (aq_row) memcpy(aq_row, aq, (size_t)I);
-    if (as_row) memcpy(as_row, as, (size_t)I / 32);
-    free(xd); free(h1); free(act); free(aq); free(as); free(ad);
-    return 0;
+    free(aq); free(as);
+    return rc;
 }
 
 static int shape_ok(const oracle_shape_t* s) {
@@ -463,4 +514,56 @@ int oracle_forward_tokens(const oracle_shape_t* s, const uint16_t* x,
     }
     free(xrow); free(xq); free(xs); free(orow); free(acc);
     return rc;
+}
+
+/* Single routed rows, for checking chosen rows of a large layer: row i is
+ * token tokens[i] of x through expert experts[i] with routing weight
+ * weights[i] -- the same quantise -> L1 -> SwiGLU*w -> requant steps as the
+ * grouped and per-token paths (a4-a7).  Writes aq_rows [n][I], as_rows
+ * [n][I/32] and, when not NULL, h1_rows [n][2I]. */
+int oracle_l1_act_rows(const oracle_shape_t* s, const uint16_t* x, const uint8_t* W1q,
+                       const uint8_t* S1, int n, const int32_t* experts, const int32_t* tokens,
+                       const float* weights, uint16_t* h1_rows, uint8_t* aq_rows,
+                       uint8_t* as_rows) {
+    if (!shape_ok(s) || n < 0) return -1;
+    const int T = s->T, H = s->H, I = s->I, E = s->E;
+    for (int i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= T || experts[i] < 0 || experts[i] >= E) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int i = 0; i < n; ++i) {
+        float* xrow = (float*)malloc((size_t)H * sizeof(float));
+        uint8_t* xq = (uint8_t*)malloc((size_t)H);
+        uint8_t* xs = (uint8_t*)malloc((size_t)H / 32);
+        if (!xrow || !xq || !xs) {
+            bad |= 1;
+        } else {
+            for (int h = 0; h < H; ++h) xrow[h] = oracle_bf16_to_f32(x[(int64_t)tokens[i] * H + h]);
+            oracle_quant_e4m3_row(xrow, H, xq, xs);
+            bad |= l1_act_row(s, experts[i], xq, xs, weights[i], W1q, S1,
+                              h1_rows ? h1_rows + (int64_t)i * 2 * I : NULL,
+                              aq_rows + (int64_t)i * I, as_rows + (int64_t)i * (I / 32), 0, 1) != 0;
+        }
+        free(xrow); free(xq); free(xs);
+    }
+    return bad ? -3 : 0;
+}
+
+/* L2 (a8) alone on given activation rows: row i is the e4m3 codes
+ * aq_rows[i] with scale bytes as_rows[i] through expert experts[i] ->
+ * o_rows [n][H] bf16.  Lets a test feed the activations a GPU produced into
+ * the exact L2, so that L2 is checked apart from the rounding of L1. */
+int oracle_l2_rows(const oracle_shape_t* s, const uint8_t* W2q, const uint8_t* S2, int n,
+                   const int32_t* experts, const uint8_t* aq_rows, const uint8_t* as_rows,
+                   uint16_t* o_rows) {
+    if (!shape_ok(s) || n < 0) return -1;
+    const int H = s->H, I = s->I, E = s->E;
+    for (int i = 0; i < n; ++i)
+        if (experts[i] < 0 || experts[i] >= E) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int i = 0; i < n; ++i)
+        bad |= l2_row(s, experts[i], aq_rows + (int64_t)i * I, as_rows + (int64_t)i * (I / 32), W2q,
+                      S2, o_rows + (int64_t)i * H, 0, 1) != 0;
+    return bad ? -3 : 0;
 }

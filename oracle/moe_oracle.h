@@ -112,6 +112,21 @@ int oracle_forward_tokens(const oracle_shape_t* s, const uint16_t* x,
                           const uint8_t* S2, int n_tokens, const int32_t* tokens,
                           uint16_t* y_rows, uint8_t* aq_slots, uint8_t* as_slots);
 
+/* ---- single routed rows (for checking chosen rows of a large layer) ----
+ * oracle_l1_act_rows: row i = token tokens[i] of x, quantised, through
+ * expert experts[i]'s L1, SwiGLU * weights[i], e4m3 requant (a4-a7) ->
+ * aq_rows [n][I], as_rows [n][I/32], optional h1_rows [n][2I] (bf16 gate|up).
+ * oracle_l2_rows: L2 alone (a8) on given activation rows: aq_rows[i] /
+ * as_rows[i] through expert experts[i] -> o_rows [n][H] bf16.
+ * Both run the same per-row steps as oracle_forward; rows in parallel. */
+int oracle_l1_act_rows(const oracle_shape_t* s, const uint16_t* x, const uint8_t* W1q,
+                       const uint8_t* S1, int n, const int32_t* experts, const int32_t* tokens,
+                       const float* weights, uint16_t* h1_rows, uint8_t* aq_rows,
+                       uint8_t* as_rows);
+int oracle_l2_rows(const oracle_shape_t* s, const uint8_t* W2q, const uint8_t* S2, int n,
+                   const int32_t* experts, const uint8_t* aq_rows, const uint8_t* as_rows,
+                   uint16_t* o_rows);
+
 /* Threads the parallel loops use (OpenMP). */
 int oracle_num_threads(void);
 

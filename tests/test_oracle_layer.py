@@ -259,3 +259,53 @@ def test_forward_empty_and_fully_masked():
     assert oracle.forward(inp).shape == (0, 64)
     inp = moe_inputs.make_inputs(T=5, H=64, I=32, E=4, K=2, routing="uniform", seed=1, mask_p=1.0)
     assert (oracle.forward(inp) == 0).all()
+
+
+# ----------------------------------------------------------------------------
+# single-row entries (used to check chosen rows of full-size GPU runs)
+# ----------------------------------------------------------------------------
+def test_row_entries_equal_grouped_path():
+    """oracle.l1_act_rows on each pool row's (token, expert, weight) and
+    oracle.l2_rows on the grouped path's activation rows reproduce the
+    grouped path's h1, act_q, act_s and L2 rows bit for bit."""
+    inp = moe_inputs.make_inputs(T=45, H=160, I=96, E=5, K=3, routing="zipf", seed=23, mask_p=0.2)
+    K, E = inp["K"], inp["E"]
+    _, mid = oracle.forward(inp, intermediates=True)
+    R = int(mid["offsets"][-1])
+    experts = np.searchsorted(mid["offsets"], np.arange(R), side="right") - 1
+    tokens = mid["pool_src"][:R] // K
+    h1, aq, as_ = oracle.l1_act_rows(inp, experts, tokens, mid["pool_w"][:R], h1=True)
+    np.testing.assert_array_equal(h1, mid["h1"][:R])
+    np.testing.assert_array_equal(aq, mid["act_q"][:R])
+    np.testing.assert_array_equal(as_, mid["act_s"][:R])
+    o = oracle.l2_rows(inp, experts, mid["act_q"][:R], mid["act_s"][:R])
+    np.testing.assert_array_equal(o, mid["o"][:R])
+    assert 0 <= experts.min() and experts.max() < E
+
+
+def test_row_entries_at_production_width_match_torch_fp64():
+    """At the production widths (H = 7168 along L1's K, I = 2048 along L2's
+    K), where the products' exponents spread furthest, the oracle's L1 rows
+    equal torch's fp64 matmul of the dequantised operands rounded fp32 ->
+    bf16, and its L2 rows on the oracle's own activations equal the same for
+    L2: the exact-sum reading holds at these sizes too."""
+    H, I = 7168, 2048
+    inp = moe_inputs.make_inputs(T=6, H=H, I=I, E=2, K=2, routing="uniform", seed=24)
+    experts = np.array([0, 1, 1, 0], np.int32)
+    tokens = np.array([0, 3, 5, 2], np.int32)
+    weights = np.array([0.61, 0.39, 1.0, 0.125], np.float32)
+    h1, aq, as_ = oracle.l1_act_rows(inp, experts, tokens, weights, h1=True)
+    o = oracle.l2_rows(inp, experts, aq, as_)
+    x = _bf16_to_torch(inp["x"]).float()
+    _, _, xd = torch_quant_e4m3(x)
+    for e in (0, 1):
+        sel = np.nonzero(experts == e)[0]
+        W1 = torch_dequant_fp4(inp["W1q"][e], inp["S1"][e])
+        h = (xd[torch.from_numpy(tokens[sel].astype(np.int64))] @ W1.T).float()
+        np.testing.assert_array_equal(h1[sel], _bf16_from_torch(h))
+        del W1
+        W2 = torch_dequant_fp4(inp["W2q"][e], inp["S2"][e])
+        ad = (torch.from_numpy(oracle.e4m3_to_f32(aq[sel]).astype(np.float64))
+              * torch.exp2(torch.from_numpy(as_[sel].astype(np.float64)) - 127).repeat_interleave(32, dim=1))
+        np.testing.assert_array_equal(o[sel], _bf16_from_torch((ad @ W2.T).float()))
+        del W2
