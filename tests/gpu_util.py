@@ -69,22 +69,3 @@ def view(workspace: torch.Tensor, inp: dict, name: str, rows: int | None = None)
         shape = (rows,) + shape[1:]
     nbytes = int(np.prod(shape)) * np.dtype(dt).itemsize
     return workspace[off:off + nbytes].cpu().numpy().view(dt).reshape(shape)
-
-
-def rel_l2_rows(y: np.ndarray, ref: np.ndarray) -> np.ndarray:
-    """Per-row relative L2 error of bf16 bit arrays."""
-    yf = (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    rf = (ref.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    num = np.linalg.norm(yf - rf, axis=1)
-    den = np.linalg.norm(rf, axis=1)
-    return np.where(den > 0, num / np.maximum(den, 1e-300), num)
-
-
-def e4m3_step_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
-    """|index difference| of two e4m3 codes on the ordered value line
-    (sign-magnitude codes mapped to a monotone integer scale)."""
-    def ordinal(c):
-        c = c.astype(np.int32)
-        mag = c & 0x7F
-        return np.where(c & 0x80, -mag, mag)
-    return np.abs(ordinal(a) - ordinal(b))

@@ -1,0 +1,65 @@
+// mfma_block.hip -- test infrastructure: one scaled MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4, A = e4m3, B = e2m1, one UE8M0 scale per
+// 32 along K on each operand) per 32 x 32 x 64 block, with a zero
+// accumulator, so that a test can compare each block's result with the exact
+// sum of its products.  Not part of the layer library.
+//
+// Operand lane layout (the same one the layer's GEMMs use):
+//  A (8 VGPRs): lane l holds row l%32; bytes 0-15 are k = 16*(l/32)+0..15,
+//    bytes 16-31 are k = 32 + 16*(l/32) + 0..15.
+//  B (4 VGPRs of 8): lane l holds column l%32, k = 32*(l/32) + 0..31, two
+//    codes per byte, even k in the low nibble.
+//  Scales: lane l gives the scale of row (column) l%32 for k-block l/32,
+//    byte 0 of its scale register.
+//  D (16 fp32): lane l, register r is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Block b: A [32 rows][64 k] e4m3 codes, B [32 columns][32 bytes] (64 e2m1
+// codes per column), sa [32 rows][2 k-blocks], sb [32 columns][2 k-blocks],
+// D [32 rows][32 columns] fp32.  One 64-lane workgroup per block.
+__global__ __launch_bounds__(64) void k_mfma_block(const uint8_t* __restrict__ A,
+                                                   const uint8_t* __restrict__ B,
+                                                   const uint8_t* __restrict__ sa,
+                                                   const uint8_t* __restrict__ sb,
+                                                   float* __restrict__ D) {
+    const int b = blockIdx.x, l = threadIdx.x;
+    const int row = l & 31, h = l >> 5;
+    const uint8_t* a = A + (size_t)b * 32 * 64 + row * 64;
+    const uint8_t* bb = B + (size_t)b * 32 * 32 + row * 32 + 16 * h;  // column l%32
+    v8i av, bv;
+    for (int d = 0; d < 4; ++d) {
+        int w0 = 0, w1 = 0;
+        for (int j = 0; j < 4; ++j) {
+            w0 |= (int)a[16 * h + 4 * d + j] << (8 * j);
+            w1 |= (int)a[32 + 16 * h + 4 * d + j] << (8 * j);
+        }
+        av[d] = w0;
+        av[4 + d] = w1;
+        int wb = 0;
+        for (int j = 0; j < 4; ++j) wb |= (int)bb[4 * d + j] << (8 * j);
+        bv[d] = wb;
+        bv[4 + d] = 0;
+    }
+    const int sA = sa[(size_t)b * 64 + row * 2 + h];
+    const int sB = sb[(size_t)b * 64 + row * 2 + h];
+    v16f c;
+    for (int r = 0; r < 16; ++r) c[r] = 0.f;
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 4, 0, sA, 0, sB);
+    for (int r = 0; r < 16; ++r) {
+        const int orow = 8 * (r >> 2) + 4 * h + (r & 3);
+        D[(size_t)b * 1024 + orow * 32 + row] = c[r];
+    }
+}
+
+extern "C" int mfma_block_run(const void* A, const void* B, const void* sa, const void* sb,
+                              void* D, int nblocks, void* stream) {
+    if (nblocks < 1 || !A || !B || !sa || !sb || !D) return -1;
+    hipLaunchKernelGGL(k_mfma_block, dim3(nblocks), dim3(64), 0, (hipStream_t)stream,
+                       (const uint8_t*)A, (const uint8_t*)B, (const uint8_t*)sa,
+                       (const uint8_t*)sb, (float*)D);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}

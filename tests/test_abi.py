@@ -72,6 +72,14 @@ def test_workspace_sizing(moe):
     assert moe.moe_workspace_bytes(T, H, I, 2000, K) == 0
     assert moe.moe_workspace_bytes(T, H, I, E, 65) == 0
     assert 0 < moe.moe_dispatch_workspace_bytes(T, H, E, K) < b
+    # shapes the fused layer refuses get no workspace size and no views, so a
+    # caller cannot size a buffer for a call that would fail
+    for bad in ((T, 7168 - 32, I, E, K), (T, H, I - 32, E, K), (1 << 20, 7168, I, E, 1)):
+        assert moe.moe_workspace_bytes(*bad) == 0, bad
+        with pytest.raises(moe.MoeError):
+            moe.moe_workspace_views(*bad)
+    # the standalone dispatch still takes any H % 32 == 0
+    assert moe.moe_dispatch_workspace_bytes(T, 7168 - 32, E, K) > 0
 
 
 def test_host_side_errors_need_no_device(moe):
