@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup-ms", type=float, default=1500.0,
+                   help="keep warming up (whole steps) until at least this much GPU time has run, "
+                        "so that the timed steps start at steady clocks")
     p.add_argument("--workload", default="prefill",
                    help="tiny | small | prefill | skewed | many")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -61,10 +64,12 @@ def parse():
     return p.parse_args()
 
 
-# HBM traffic of the L1 GEMM per launch, from two rocprofv3 --pmc passes
-# (FETCH_SIZE, WRITE_SIZE) scaled by a plain copy of known size.  The summary
-# names the sha256 of the GEMM sources it was measured on; a changed kernel
-# reports null.
+# Bytes the L1 GEMM moves across its XCDs' L2 boundary per launch (reads
+# that leave the L2 for the fabric -- Infinity Cache hits included -- plus
+# writes), from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by
+# a plain copy of known size.  This is an upper bound on its HBM bytes, not
+# HBM bytes themselves.  The summary names the sha256 of the GEMM sources it
+# was measured on; a changed kernel reports null.
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_l1_prefill_hbm_traffic.md")
 GEMM_SOURCES = ("combine_dispatch_amd/csrc/gemm.hip", "combine_dispatch_amd/csrc/moe_kernels.hpp",
                 "combine_dispatch_amd/csrc/moe_device.hpp")
@@ -90,7 +95,7 @@ def measured_traffic(workload: str):
     if fields.get("gemm_source_sha256") != gemm_source_hash():
         return None
     try:
-        return int(float(fields["hbm_bytes_per_launch"]))
+        return int(float(fields["fabric_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
 
@@ -144,9 +149,18 @@ def main():
     step, other = ((step_packed, step_canonical) if a.scales == "packed"
                    else (step_canonical, step_packed))
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
+    # warm-up: at least `warmup` steps and at least `warmup_ms` of GPU time
+    # (the clocks take a few hundred milliseconds of load to settle)
+    warm_steps = 0
+    w0 = time.perf_counter()
+    while True:
+        for _ in range(max(a.warmup, 1)):
+            step()
+        warm_steps += max(a.warmup, 1)
+        torch.cuda.synchronize()
+        if warm_steps >= a.warmup and (time.perf_counter() - w0) * 1e3 >= a.warmup_ms:
+            break
+    warm_s = time.perf_counter() - w0
 
     # timed region: exactly `steps` whole-layer steps, nothing else on the
     # stream between them
@@ -260,6 +274,8 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
+        "warmup_steps_run": warm_steps,
+        "warmup_s": round(warm_s, 3),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -275,7 +291,10 @@ def main():
         "frac_of_fp8_peak": round(tflops / PEAK_TFLOPS, 4),
         "roofline": {"bound": "mfma", "kernel": "gemm_l1", "achieved": round(l1_tflops, 2),
                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(l1_tflops / PEAK_TFLOPS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     "traffic_kind": "bytes across the XCD L2 boundary per launch "
+                                     "(FETCH_SIZE x2 + WRITE_SIZE, Infinity Cache hits included): "
+                                     "an upper bound on HBM bytes"},
         "kernels_ms_per_launch": {k: round(v, 4) for k, v in per_launch.items()},
         "ms_per_step_with_kernel_events": round(ms_per_step_events, 4),
         "kernels": {
@@ -321,8 +340,23 @@ def cpu_baseline(inp, budget_s: float) -> dict:
     return {"value": round(flop / el / 1e12, 6), "unit": "TFLOP/s",
             "routed_rows_per_s": round(routes / el, 3), "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{done_tok} tokens ({routes} routed rows) of the same workload, "
-                      f"per-token brute-force path, {el:.1f} s"}
+            "sample": f"{done_tok} whole tokens ({routes} routed rows) of the same workload, drawn "
+                      f"at random, each through the oracle's per-token path (quantise, L1, "
+                      f"SwiGLU*w, requant, L2 per route, fp32 combine; the same arithmetic as its "
+                      f"grouped path), {el:.1f} s; rate scaled to the workload by routed rows",
+            "threads_kind": "OpenMP threads of the oracle's parallel loops",
+            "nproc": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 if __name__ == "__main__":

@@ -34,6 +34,14 @@ bool shape_basic_ok(const moe_shape_t* s) {
            s->K <= 64 && (int64_t)s->T * s->K < (int64_t(1) << 31);
 }
 
+// Shapes the fused layer's GEMM tiling takes: H a multiple of the 256-column
+// tile (L2 N) and of the 128-wide K step (L1 K), I a multiple of 128 (L1 N
+// in gate/up halves of 128, L2 K step), and 32-bit token-row offsets.
+bool fused_shape_ok(const moe_shape_t* s) {
+    return shape_basic_ok(s) && s->H % kBN == 0 && s->I % 128 == 0 &&
+           (int64_t)s->T * s->H < (int64_t(1) << 32);
+}
+
 // Workspace regions, in order.  The routing scratch comes first so that
 // moe_dispatch can use a prefix of the same layout.
 Layout make_layout(const moe_shape_t* s) {
@@ -213,7 +221,7 @@ moe_options_t moe_default_options(void) {
 }
 
 size_t moe_workspace_bytes(const moe_shape_t* s) {
-    if (!shape_basic_ok(s) || s->H % 32 || s->I % 32) return 0;
+    if (!fused_shape_ok(s)) return 0;
     return make_layout(s).total;
 }
 
@@ -226,7 +234,7 @@ size_t moe_dispatch_workspace_bytes(const moe_shape_t* s) {
 
 int moe_workspace_views(const moe_shape_t* s, moe_workspace_views_t* v) {
     if (!v) return MOE_ERR_INVALID_ARG;
-    if (!shape_basic_ok(s) || s->H % 32 || s->I % 32) {
+    if (!fused_shape_ok(s)) {
         memset(v, 0xFF, sizeof *v);
         return MOE_ERR_INVALID_ARG;
     }
@@ -273,8 +281,7 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     if (!shape_basic_ok(s)) return MOE_ERR_INVALID_ARG;
     const moe_options_t o = opt ? *opt : moe_default_options();
     if (!isnan(o.activation_clamp)) return MOE_ERR_UNSUPPORTED;
-    if (s->H % kBN || s->I % 128) return MOE_ERR_UNSUPPORTED;
-    if ((int64_t)s->T * s->H >= (int64_t(1) << 32)) return MOE_ERR_UNSUPPORTED;  // 32-bit row offsets
+    if (!fused_shape_ok(s)) return MOE_ERR_UNSUPPORTED;
     if (s->T == 0) return MOE_OK;
     if (!x || !topk_idx || !topk_w || !W1q || !W2q || !y) return MOE_ERR_INVALID_ARG;
     if (packed) {
@@ -397,7 +404,7 @@ int moe_fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void
 }
 
 size_t moe_packed_scales_bytes(const moe_shape_t* s) {
-    if (!shape_basic_ok(s) || s->H % kBN || s->I % 128) return 0;
+    if (!shape_basic_ok(s) || s->H % kBN || s->I % 128) return 0;  // T is not used here
     return packed_total_bytes(s);
 }
 

@@ -127,7 +127,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // data lands at LDS address m0 + 16 l (4 l).  Written as inline asm so that
 // the compiler neither reorders LDS reads around them nor inserts its own
 // conservative vmcnt waits; the main loop counts them itself.  M0 is set
-// here; no compiler-generated code in these kernels reads M0.
+// here.  The compiler treats M0 as a reserved register (a clobber of it is
+// ignored), so nothing else may use M0 in these kernels: a test over the
+// assembly of the build checks that every instruction reading M0 follows
+// one of these moves directly.
 // The asm operands must sit in SGPRs; the values are wave-uniform by
 // construction and readfirstlane states that to the compiler (free when it
 // already knows).

@@ -77,7 +77,9 @@ enum { MOE_PAYLOAD_FP8_E4M3 = 0, MOE_PAYLOAD_BF16 = 1 };
 moe_options_t moe_default_options(void);
 
 /* Bytes of device workspace moe_fused_forward needs for shape *s (capacity
- * T*K routed rows plus tile padding).  Host only; 0 on a bad shape. */
+ * T*K routed rows plus tile padding).  Host only; 0 on a shape that
+ * moe_fused_forward would refuse (H % 256, I % 128, T * H >= 2^32, or the
+ * basic limits). */
 size_t moe_workspace_bytes(const moe_shape_t* s);
 
 /* Bytes of device workspace moe_dispatch needs (routing scratch only). */
@@ -184,7 +186,8 @@ int moe_combine(const moe_shape_t* s, const void* pool_out, const int32_t* slot_
                 const float* topk_w, void* y, moe_stream_t stream);
 
 /* Byte offsets of intermediates inside a moe_fused_forward workspace, so that
- * tests can read them after a call (all -1 on a bad shape).
+ * tests can read them after a call (all -1 and MOE_ERR_INVALID_ARG on a shape
+ * moe_fused_forward would refuse).
  * The fused layer quantises every token row once (x_q, token-major) and its
  * L1 GEMM reads pool row r from token row pool_tok[r]; the expert-major pool
  * itself is not materialised (moe_dispatch materialises it).
