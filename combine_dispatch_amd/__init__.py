@@ -5,7 +5,8 @@ Every step of the MoE layer runs in the HIP kernels behind the C ABI in
 current HIP stream through ctypes.  There is no fallback: if the library is
 missing or the device is not gfx950 the calls raise.
 
-Names match the C entry points: ``moe_fused_forward``, ``moe_dispatch``,
+Names match the C entry points: ``moe_fused_forward``,
+``moe_fused_forward_packed``, ``moe_fused_forward_packed_noalloc``, ``moe_dispatch``,
 ``moe_combine``, ``moe_workspace_bytes``, ``moe_dispatch_workspace_bytes``,
 ``moe_workspace_views``, ``moe_status_string``.
 """
@@ -24,6 +25,8 @@ MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_DEVICE = -4
 MOE_ERR_BAD_ROUTING = -5
+MOE_ERR_TOO_LARGE = -6
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_PAYLOAD_FP8_E4M3 = 0
 MOE_PAYLOAD_BF16 = 1
 
@@ -31,7 +34,7 @@ EXPORTED = ("moe_default_options", "moe_workspace_bytes", "moe_dispatch_workspac
             "moe_fused_forward", "moe_dispatch", "moe_combine", "moe_workspace_views",
             "moe_status_string", "moe_profile_start", "moe_profile_stop",
             "moe_profile_stage_name", "moe_packed_scales_bytes", "moe_pack_weight_scales",
-            "moe_fused_forward_packed")
+            "moe_fused_forward_packed", "moe_fused_forward_packed_noalloc")
 PROFILE_STAGES = 8
 
 
@@ -84,6 +87,9 @@ def lib():
         L.moe_fused_forward_packed.argtypes = [shp, ctypes.POINTER(MoeOptions), vp, vp, vp, vp,
                                                vp, vp, vp, vp, sz, vp]
         L.moe_fused_forward_packed.restype = i32
+        L.moe_fused_forward_packed_noalloc.argtypes = [shp, ctypes.POINTER(MoeOptions), vp, vp, vp,
+                                                       vp, vp, vp, vp, vp]
+        L.moe_fused_forward_packed_noalloc.restype = i32
         L.moe_dispatch.argtypes = [shp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_dispatch.restype = i32
         L.moe_combine.argtypes = [shp, vp, vp, vp, vp, vp]
@@ -193,6 +199,24 @@ def moe_fused_forward_packed(x, topk_idx, topk_w, W1q, W2q, packed, y, workspace
                                           _ptr(y), _ptr(workspace),
                                           workspace.numel() * workspace.element_size(),
                                           _stream(stream)), "moe_fused_forward_packed")
+
+
+def moe_fused_forward_packed_noalloc(x, topk_idx, topk_w, W1q, W2q, packed, y, opts=None,
+                                     stream=None, E: int | None = None,
+                                     I: int | None = None) -> None:
+    """moe_fused_forward_packed with the library's own device scratch as the
+    workspace (no allocation in the call; shapes whose moe_workspace_bytes
+    exceeds MOE_NOALLOC_SCRATCH_BYTES raise MoeError MOE_ERR_TOO_LARGE)."""
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    E = W1q.shape[0] if E is None else E
+    I = W2q.shape[2] * 2 if I is None else I
+    shape = MoeShape(T, H, I, E, K)
+    o = ctypes.byref(opts) if opts is not None else None
+    _check(lib().moe_fused_forward_packed_noalloc(ctypes.byref(shape), o, _ptr(x), _ptr(topk_idx),
+                                                  _ptr(topk_w), _ptr(W1q), _ptr(W2q), _ptr(packed),
+                                                  _ptr(y), _stream(stream)),
+           "moe_fused_forward_packed_noalloc")
 
 
 def moe_dispatch(x, topk_idx, topk_w, E: int, payload: int, counts, offsets, pool_src,

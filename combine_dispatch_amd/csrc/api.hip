@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/moe.h"
@@ -199,6 +200,30 @@ int run_routing(const moe_shape_t* s, const Layout& L, const int64_t* topk_idx, 
     return launch_status();
 }
 
+// ---- the allocation-free entry's workspace ---------------------------------
+// A file-scope device array: every GPU the library runs on holds its own copy
+// for the life of the process.  In host code `scratch` names a host-side
+// stand-in, not device memory, so host code uses only the address that
+// hipGetSymbolAddress returns for the current device (scratch_device_ptr).
+constexpr size_t kNoAllocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+void* scratch_device_ptr() {
+    static std::mutex mu;
+    static void* ptrs[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        ptrs[dev] = p;
+    }
+    return ptrs[dev];
+}
+
 int check_routing_flag(uint8_t* ws, const Layout& L, hipStream_t stream) {
     int32_t flag = 0;
     if (hipMemcpyAsync(&flag, ws + L.err_flag, sizeof flag, hipMemcpyDeviceToHost, stream) !=
@@ -263,6 +288,9 @@ const char* moe_status_string(int status) {
         case MOE_ERR_WORKSPACE: return "workspace missing or too small";
         case MOE_ERR_DEVICE: return "device is not gfx950 or a kernel launch failed";
         case MOE_ERR_BAD_ROUTING: return "an expert index was >= E";
+        case MOE_ERR_TOO_LARGE:
+            return "shape needs more workspace than the allocation-free entry's device scratch holds "
+                   "(moe_workspace_bytes(s) > MOE_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -432,6 +460,26 @@ int moe_fused_forward_packed(const moe_shape_t* s, const moe_options_t* opt, con
     return fused_forward(s, opt, x, topk_idx, topk_w, W1q, nullptr, W2q, nullptr,
                          static_cast<const uint8_t*>(packed_scales), y, workspace,
                          workspace_bytes, stream);
+}
+
+int moe_fused_forward_packed_noalloc(const moe_shape_t* s, const moe_options_t* opt,
+                                     const void* x, const int64_t* topk_idx, const float* topk_w,
+                                     const uint8_t* W1q, const uint8_t* W2q,
+                                     const void* packed_scales, void* y, moe_stream_t stream) {
+    if (!packed_scales) return MOE_ERR_INVALID_ARG;
+    // the limit is checked on the host, before anything touches the device
+    if (shape_basic_ok(s) && fused_shape_ok(s) && s->T > 0 &&
+        make_layout(s).total > kNoAllocScratchBytes)
+        return MOE_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    if (shape_basic_ok(s) && fused_shape_ok(s) && s->T > 0) {
+        if (!device_ok()) return MOE_ERR_DEVICE;
+        ws = scratch_device_ptr();
+        if (!ws) return MOE_ERR_DEVICE;
+    }
+    return fused_forward(s, opt, x, topk_idx, topk_w, W1q, nullptr, W2q, nullptr,
+                         static_cast<const uint8_t*>(packed_scales), y, ws,
+                         ws ? kNoAllocScratchBytes : 0, stream);
 }
 
 int moe_dispatch(const moe_shape_t* s, const void* x, const int64_t* topk_idx, const float* topk_w,

@@ -68,7 +68,9 @@ enum {
     MOE_ERR_UNSUPPORTED = -2, /* shape outside the kernels' tiling, option not implemented */
     MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
     MOE_ERR_DEVICE = -4,      /* not a gfx950 device, or a launch failed */
-    MOE_ERR_BAD_ROUTING = -5  /* debug_validate found an expert index >= E */
+    MOE_ERR_BAD_ROUTING = -5, /* debug_validate found an expert index >= E */
+    MOE_ERR_TOO_LARGE = -6    /* moe_fused_forward_packed_noalloc: the shape's workspace
+                                 exceeds MOE_NOALLOC_SCRATCH_BYTES */
 };
 
 enum { MOE_PAYLOAD_FP8_E4M3 = 0, MOE_PAYLOAD_BF16 = 1 };
@@ -146,6 +148,29 @@ int moe_fused_forward_packed(const moe_shape_t* s, const moe_options_t* opt /* N
                              const uint8_t* W1q, const uint8_t* W2q, const void* packed_scales,
                              void* y, void* workspace, size_t workspace_bytes,
                              moe_stream_t stream);
+
+/*
+ * moe_fused_forward_packed without a workspace argument, for callers that
+ * cannot allocate device memory around the call: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The
+ * workspace is a device array inside the library, MOE_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU, which every GPU the library runs on holds until the
+ * process ends; the call itself allocates nothing.  Inputs, outputs and the
+ * packed weight scales are the caller's, as in moe_fused_forward_packed, and
+ * the result is bit-identical to it.
+ * Limit: shapes with moe_workspace_bytes(s) > MOE_NOALLOC_SCRATCH_BYTES get
+ * MOE_ERR_TOO_LARGE before anything is launched (decode and small batches
+ * fit: at H = 7168, I = 2048, E = 32 up to about 2000 routed rows T*K).
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (different streams, threads or processes' streams sharing the
+ * library instance) race and give wrong results; calls ordered on one
+ * stream are fine (the array's contents on entry do not matter).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_fused_forward_packed_noalloc(const moe_shape_t* s, const moe_options_t* opt /* NULL = defaults */,
+                                     const void* x, const int64_t* topk_idx, const float* topk_w,
+                                     const uint8_t* W1q, const uint8_t* W2q,
+                                     const void* packed_scales, void* y, moe_stream_t stream);
 
 /*
  * Dispatch only: routing metadata plus the expert-major pool.  [P3] sections

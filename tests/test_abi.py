@@ -128,3 +128,22 @@ def test_packed_scale_entry_points_host_side(moe):
     assert L.moe_fused_forward_packed(ctypes.byref(moe.MoeShape(0, 256, 128, 4, 2)), None,
                                       *[null] * 5, ctypes.c_void_p(256), null, null, 0,
                                       null) == moe.MOE_OK
+
+
+def test_noalloc_entry_host_side(moe):
+    """The allocation-free entry refuses shapes whose workspace exceeds its
+    device scratch before touching the device, and takes T == 0 as a no-op."""
+    L = moe.lib()
+    null = ctypes.c_void_p(0)
+    one = ctypes.c_void_p(256)
+    big = moe.MoeShape(8192, 7168, 2048, 32, 8)
+    assert moe.moe_workspace_bytes(8192, 7168, 2048, 32, 8) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert L.moe_fused_forward_packed_noalloc(ctypes.byref(big), None, *[one] * 6, one,
+                                              null) == moe.MOE_ERR_TOO_LARGE
+    assert "scratch" in moe.moe_status_string(moe.MOE_ERR_TOO_LARGE)
+    assert L.moe_fused_forward_packed_noalloc(ctypes.byref(moe.MoeShape(0, 256, 128, 4, 2)), None,
+                                              *[null] * 5, one, null, null) == moe.MOE_OK
+    assert L.moe_fused_forward_packed_noalloc(ctypes.byref(big), None, *[one] * 5, null, one,
+                                              null) == moe.MOE_ERR_INVALID_ARG
+    # decode-sized shapes fit
+    assert moe.moe_workspace_bytes(128, 7168, 2048, 32, 8) <= moe.MOE_NOALLOC_SCRATCH_BYTES
