@@ -20,7 +20,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t seg_hist, seg_base, seg_err, counts, offsets, mtiles, num_mtiles, err_flag;
+    size_t seg_hist, seg_base, seg_err, blk_hist, blk_err, counts, offsets, mtiles, num_mtiles,
+        err_flag;
     size_t pool_src, slot_to_pool, pool_w, pool_tok, x_q, pool_s, act_q, act_s, l2_out, s1t, s2t,
         tok_s;
     size_t routing_end;  // bytes moe_dispatch needs
@@ -61,6 +62,9 @@ Layout make_layout(const moe_shape_t* s) {
     L.seg_hist = take(sizeof(int32_t) * L.nseg * E);
     L.seg_base = take(sizeof(int32_t) * L.nseg * E);
     L.seg_err = take(sizeof(int32_t) * (L.nseg + 1));
+    const int64_t nblk = (L.nseg + kRouteWaves - 1) / kRouteWaves;
+    L.blk_hist = take(sizeof(int32_t) * nblk * E);
+    L.blk_err = take(sizeof(int32_t) * (nblk + 1));
     L.mtiles = take(sizeof(MTile) * L.max_mtiles);
     L.num_mtiles = take(sizeof(int32_t));
     L.err_flag = take(sizeof(int32_t));
@@ -168,14 +172,20 @@ int bits_for(int E) {
     return b < 1 ? 1 : b;
 }
 
-// a1-a3 into caller-visible arrays; the segment scratch lives at ws.
-// a1 (unless the caller's first launch already ran it), a2, a3.
+// a1-a3 into caller-visible arrays; the routing scratch lives at ws.
 int route_blocks(const Layout& L) { return (int)((L.nseg + kRouteWaves - 1) / kRouteWaves); }
 
+// One-launch routing (k_route) while every block can afford to read all the
+// block histograms; otherwise a single-block scan, then the scatter.
+bool route_fused(const Layout& L, int E) { return (int64_t)route_blocks(L) * E <= kRouteFusedMax; }
+
+// a1 (unless the caller's first launch already counted: `counted`), a2, a3,
+// and, with pool_s set, the pool rows' A-scale words gathered from the
+// token words tok_s ([T][W]) into the GEMM's packed k-major layout.
 int run_routing(const moe_shape_t* s, const Layout& L, const int64_t* topk_idx, const float* topk_w,
                 uint8_t* ws, int32_t* pool_tok, int32_t* counts, int32_t* offsets, int32_t* pool_src,
-                int32_t* slot_to_pool, float* pool_w, hipStream_t stream, bool counted,
-                int pc = -1) {
+                int32_t* slot_to_pool, float* pool_w, hipStream_t stream, bool counted, int pc,
+                const uint32_t* tok_s, uint32_t* pool_s) {
     const int64_t TK = (int64_t)s->T * s->K;
     const int E = s->E;
     const int nblk = route_blocks(L);
@@ -183,9 +193,31 @@ int run_routing(const moe_shape_t* s, const Layout& L, const int64_t* topk_idx, 
     int32_t* seg_hist = reinterpret_cast<int32_t*>(ws + L.seg_hist);
     int32_t* seg_base = reinterpret_cast<int32_t*>(ws + L.seg_base);
     int32_t* seg_err = reinterpret_cast<int32_t*>(ws + L.seg_err);
-    if (!counted)
+    int32_t* blk_hist = reinterpret_cast<int32_t*>(ws + L.blk_hist);
+    int32_t* blk_err = reinterpret_cast<int32_t*>(ws + L.blk_err);
+    const bool fused = route_fused(L, E);
+    if (!counted && nblk > 0)
         hipLaunchKernelGGL(k_route_count, dim3(nblk), dim3(kRouteThreads), lds, stream, topk_idx,
-                           TK, E, seg_hist, seg_err);
+                           TK, E, seg_hist, seg_err, fused ? blk_hist : static_cast<int32_t*>(nullptr),
+                           blk_err);
+    if (fused) {
+        hipLaunchKernelGGL(k_route, dim3((unsigned)(nblk > 0 ? nblk : 1)), dim3(kRouteThreads),
+                           route_lds_bytes(E), stream, topk_idx, topk_w, TK, E, bits_for(E), s->K,
+                           blk_hist, blk_err, nblk, counts, offsets,
+                           reinterpret_cast<MTile*>(ws + L.mtiles),
+                           reinterpret_cast<int32_t*>(ws + L.num_mtiles),
+                           reinterpret_cast<int32_t*>(ws + L.err_flag), pool_src, slot_to_pool, pool_w,
+                           pool_tok, tok_s, s->H / 128, (int64_t)L.cap,
+                           static_cast<uint32_t*>(nullptr));
+        prof_mark(pc, MOE_STAGE_ROUTE_SCAN, stream);
+        prof_mark(pc, MOE_STAGE_ROUTE_SCATTER, stream);
+        // the scale words are a grid-wide copy (megabytes): a kernel of their own
+        if (pool_s)
+            hipLaunchKernelGGL(k_pool_scales, dim3((unsigned)((L.cap + 255) / 256)), dim3(256), 0,
+                               stream, tok_s, s->H / 128, pool_tok, offsets, s->E, (int64_t)L.cap, pool_s);
+        prof_mark(pc, MOE_STAGE_POOL_SCALES, stream);
+        return launch_status();
+    }
     const int scan_threads = 1024;  // several threads per expert split the segments
     hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(scan_threads), 0, stream, seg_hist, seg_err,
                        (int)L.nseg, E, seg_base, counts, offsets,
@@ -193,11 +225,25 @@ int run_routing(const moe_shape_t* s, const Layout& L, const int64_t* topk_idx, 
                        reinterpret_cast<int32_t*>(ws + L.num_mtiles),
                        reinterpret_cast<int32_t*>(ws + L.err_flag));
     prof_mark(pc, MOE_STAGE_ROUTE_SCAN, stream);
-    hipLaunchKernelGGL(k_route_scatter, dim3(nblk), dim3(kRouteThreads), lds, stream, topk_idx,
-                       topk_w, TK, E, bits_for(E), s->K, seg_base, pool_src, slot_to_pool, pool_w,
-                       pool_tok);
+    if (nblk > 0)
+        hipLaunchKernelGGL(k_route_scatter, dim3(nblk), dim3(kRouteThreads), lds, stream, topk_idx,
+                           topk_w, TK, E, bits_for(E), s->K, seg_base, pool_src, slot_to_pool, pool_w,
+                           pool_tok);
     prof_mark(pc, MOE_STAGE_ROUTE_SCATTER, stream);
+    if (pool_s)
+        hipLaunchKernelGGL(k_pool_scales, dim3((unsigned)((L.cap + 255) / 256)), dim3(256), 0,
+                           stream, tok_s, s->H / 128, pool_tok, offsets, s->E, (int64_t)L.cap, pool_s);
+    prof_mark(pc, MOE_STAGE_POOL_SCALES, stream);
     return launch_status();
+}
+
+int check_routing_flag(uint8_t* ws, const Layout& L, hipStream_t stream) {
+    int32_t flag = 0;
+    if (hipMemcpyAsync(&flag, ws + L.err_flag, sizeof flag, hipMemcpyDeviceToHost, stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return MOE_ERR_DEVICE;
+    return flag ? MOE_ERR_BAD_ROUTING : MOE_OK;
 }
 
 // ---- the allocation-free entry's workspace ---------------------------------
@@ -224,14 +270,6 @@ void* scratch_device_ptr() {
     return ptrs[dev];
 }
 
-int check_routing_flag(uint8_t* ws, const Layout& L, hipStream_t stream) {
-    int32_t flag = 0;
-    if (hipMemcpyAsync(&flag, ws + L.err_flag, sizeof flag, hipMemcpyDeviceToHost, stream) !=
-            hipSuccess ||
-        hipStreamSynchronize(stream) != hipSuccess)
-        return MOE_ERR_DEVICE;
-    return flag ? MOE_ERR_BAD_ROUTING : MOE_OK;
-}
 
 }  // namespace
 
@@ -357,18 +395,17 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
                            sizeof(int32_t) * kRouteWaves * s->E, stream,
                            static_cast<const uint16_t*>(x), (int64_t)T, H, tpb, x_q, tok_s, topk_idx,
                            (int64_t)T * K, s->E, ncount, reinterpret_cast<int32_t*>(ws + L.seg_hist),
-                           reinterpret_cast<int32_t*>(ws + L.seg_err));
+                           reinterpret_cast<int32_t*>(ws + L.seg_err),
+                           route_fused(L, s->E) ? reinterpret_cast<int32_t*>(ws + L.blk_hist)
+                                                : static_cast<int32_t*>(nullptr),
+                           reinterpret_cast<int32_t*>(ws + L.blk_err));
     }
     prof_mark(pc, MOE_STAGE_DISPATCH, stream);
     int rc = run_routing(s, L, topk_idx, topk_w, ws, pool_tok, counts, offsets, pool_src,
-                         slot_to_pool, pool_w, stream, true, pc);
+                         slot_to_pool, pool_w, stream, true, pc,
+                         reinterpret_cast<const uint32_t*>(tok_s), reinterpret_cast<uint32_t*>(pool_s));
     if (rc) return rc;
     if (o.debug_validate && (rc = check_routing_flag(ws, L, stream))) return rc;
-
-    hipLaunchKernelGGL(k_pool_scales, dim3((unsigned)((L.cap + 255) / 256)), dim3(256), 0,
-                       stream, reinterpret_cast<const uint32_t*>(tok_s), H / 128, pool_tok, offsets,
-                       s->E, (int64_t)L.cap, reinterpret_cast<uint32_t*>(pool_s));
-    prof_mark(pc, MOE_STAGE_POOL_SCALES, stream);
 
     GemmArgs g1;
     memset(&g1, 0, sizeof g1);
@@ -518,7 +555,7 @@ int moe_dispatch(const moe_shape_t* s, const void* x, const int64_t* topk_idx, c
     if (!device_ok()) return MOE_ERR_DEVICE;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     int rc = run_routing(s, L, topk_idx, topk_w, ws, nullptr, counts, offsets, pool_src, slot_to_pool,
-                         pool_w, stream, false);
+                         pool_w, stream, false, -1, nullptr, nullptr);
     if (rc) return rc;
     const int tpb = tokens_per_block(s->H);
     if (payload == MOE_PAYLOAD_FP8_E4M3)

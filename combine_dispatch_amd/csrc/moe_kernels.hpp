@@ -65,7 +65,21 @@ struct GemmArgs {
 };
 
 __global__ void k_route_count(const int64_t* __restrict__ topk_idx, int64_t TK, int E,
-                              int32_t* __restrict__ seg_hist, int32_t* __restrict__ seg_err);
+                              int32_t* __restrict__ seg_hist, int32_t* __restrict__ seg_err,
+                              int32_t* __restrict__ blk_hist, int32_t* __restrict__ blk_err);
+// One-launch routing (see route.hip); used while nblk * E <= kRouteFusedMax,
+// since every block reads all nblk rows of the block histograms.
+constexpr int64_t kRouteFusedMax = 1 << 16;
+inline size_t route_lds_bytes(int E) { return sizeof(int32_t) * 8 * (size_t)E + 8 * kRouteWaves * kSegSlots; }
+__global__ void k_route(const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
+                        int64_t TK, int E, int nbits, int K, const int32_t* __restrict__ blk_hist,
+                        const int32_t* __restrict__ blk_err, int nblk, int32_t* __restrict__ counts,
+                        int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
+                        int32_t* __restrict__ num_mtiles, int32_t* __restrict__ err_flag,
+                        int32_t* __restrict__ pool_src, int32_t* __restrict__ slot_to_pool,
+                        float* __restrict__ pool_w, int32_t* __restrict__ pool_tok,
+                        const uint32_t* __restrict__ tok_s, int W, int64_t cap,
+                        uint32_t* __restrict__ pool_s);
 __global__ void k_route_scan(const int32_t* __restrict__ seg_hist,
                              const int32_t* __restrict__ seg_err, int nseg, int E,
                              int32_t* __restrict__ seg_base, int32_t* __restrict__ counts,
@@ -83,7 +97,8 @@ __global__ void k_dispatch_fp8(const uint16_t* __restrict__ x, int64_t T, int H,
 __global__ void k_quantise_count(const uint16_t* __restrict__ x, int64_t T, int H, int tpb,
                                  uint8_t* __restrict__ x_q, uint8_t* __restrict__ tok_s,
                                  const int64_t* __restrict__ topk_idx, int64_t TK, int E, int ncount,
-                                 int32_t* __restrict__ seg_hist, int32_t* __restrict__ seg_err);
+                                 int32_t* __restrict__ seg_hist, int32_t* __restrict__ seg_err,
+                                 int32_t* __restrict__ blk_hist, int32_t* __restrict__ blk_err);
 __global__ void k_pool_scales(const uint32_t* __restrict__ tok_s, int W,
                               const int32_t* __restrict__ pool_tok,
                               const int32_t* __restrict__ offsets, int E, int64_t cap,

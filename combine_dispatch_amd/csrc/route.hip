@@ -24,7 +24,9 @@ namespace moe {
 __device__ __forceinline__ void route_count_block(const int64_t* __restrict__ topk_idx, int64_t TK,
                                                   int E, int32_t* __restrict__ seg_hist,
                                                   int32_t* __restrict__ seg_err, int64_t blk,
-                                                  int32_t* lds_hist /* [kRouteWaves][E] */) {
+                                                  int32_t* lds_hist /* [kRouteWaves][E] */,
+                                                  int32_t* __restrict__ blk_hist = nullptr,
+                                                  int32_t* __restrict__ blk_err = nullptr) {
     const int wv = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int64_t nseg = (TK + kSegSlots - 1) / kSegSlots;
     const int64_t seg = blk * kRouteWaves + wv;
@@ -45,6 +47,22 @@ __device__ __forceinline__ void route_count_block(const int64_t* __restrict__ to
         }
     }
     __syncthreads();
+    if (blk_hist) {
+        // the block's four segments summed: one histogram row per block
+        __shared__ int32_t s_bad;
+        if (threadIdx.x == 0) s_bad = 0;
+        __syncthreads();
+        if (bad) s_bad = 1;
+        for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+            int sum = 0;
+#pragma unroll
+            for (int w = 0; w < kRouteWaves; ++w) sum += lds_hist[w * E + e];
+            blk_hist[blk * E + e] = sum;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) blk_err[blk] = s_bad;
+        return;
+    }
     if (seg < nseg) {
         for (int e = lane; e < E; e += kWave) seg_hist[seg * E + e] = h[e];
         const unsigned long long any_bad = __ballot(bad);
@@ -54,9 +72,9 @@ __device__ __forceinline__ void route_count_block(const int64_t* __restrict__ to
 
 __global__ __launch_bounds__(kRouteThreads) void k_route_count(
     const int64_t* __restrict__ topk_idx, int64_t TK, int E, int32_t* __restrict__ seg_hist,
-    int32_t* __restrict__ seg_err) {
+    int32_t* __restrict__ seg_err, int32_t* __restrict__ blk_hist, int32_t* __restrict__ blk_err) {
     extern __shared__ int32_t lds_hist[];  // [kRouteWaves][E]
-    route_count_block(topk_idx, TK, E, seg_hist, seg_err, blockIdx.x, lds_hist);
+    route_count_block(topk_idx, TK, E, seg_hist, seg_err, blockIdx.x, lds_hist, blk_hist, blk_err);
 }
 
 // a2: exclusive prefix sum.  One block.  The segment histogram [nseg][E] is
@@ -214,6 +232,258 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(
     }
 }
 
+// Block-wide exclusive scan of v over the block's threads (kRouteThreads);
+// returns the thread's exclusive prefix and sets *total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* total, int32_t* s_w /* [kRouteWaves] */) {
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    int inc = v;
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int a = __shfl_up(inc, d);
+        if (lane >= d) inc += a;
+    }
+    __syncthreads();  // s_w free
+    if (lane == kWave - 1) s_w[wv] = inc;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int i = 0; i < kRouteWaves; ++i) {
+        if (i < wv) base += s_w[i];
+        tot += s_w[i];
+    }
+    *total = tot;
+    return base + inc - v;
+}
+
+// a2 + a3 + the pool rows' scale words, in one launch.  Block b takes the
+// kRouteWaves segments the counting pass's block b counted (wave w: segment
+// kRouteWaves*b + w) and works out for itself what a scan over that pass's
+// per-block histograms blk_hist [nblk][E] gives it -- each expert's total
+// (hence offsets[E+1]) and its rows in blocks before b -- so that no block
+// waits for another.  Then, as in the counting-sort dispatch the pages
+// describe: the per-segment base of every expert, the stable rank of every
+// valid slot inside its expert (lanes holding the same expert find each
+// other with one ballot per index bit; lower lanes first), and the pool row
+// of every slot.  With pool_s set, the block then copies the A-scale words of
+// its pool rows from their tokens' words (tok_s, [T][W]) into the GEMM's
+// packed k-major layout (word (w, r) at w * cap + r), one thread per row in
+// the order of the rows.  Block 0 also writes counts, offsets, the GEMM's
+// expert-major m-tile table and the routing error flag.
+__global__ __launch_bounds__(kRouteThreads) void k_route(
+    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int64_t TK, int E,
+    int nbits, int K, const int32_t* __restrict__ blk_hist, const int32_t* __restrict__ blk_err,
+    int nblk, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    MTile* __restrict__ mtiles, int32_t* __restrict__ num_mtiles, int32_t* __restrict__ err_flag,
+    int32_t* __restrict__ pool_src, int32_t* __restrict__ slot_to_pool, float* __restrict__ pool_w,
+    int32_t* __restrict__ pool_tok, const uint32_t* __restrict__ tok_s, int W, int64_t cap,
+    uint32_t* __restrict__ pool_s) {
+    extern __shared__ int32_t lds[];
+    int32_t* s_tot = lds;                     // [E] expert totals
+    int32_t* s_pre = s_tot + E;               // [E] rows of the expert in blocks before this one
+    int32_t* s_run = s_pre + E;               // [kRouteWaves][E] per-wave counts, then running bases
+    int32_t* s_off = s_run + kRouteWaves * E; // [E] offsets
+    int32_t* s_loc = s_off + E;               // [E] first slot of the expert in this block's row list
+    int2* s_rows = reinterpret_cast<int2*>(s_loc + E);  // [kRouteWaves * kSegSlots] (row, token)
+    __shared__ int32_t s_part[2][kRouteThreads];
+    __shared__ int32_t s_w[kRouteWaves];
+    __shared__ int32_t s_nrows;
+    const int tid = threadIdx.x, wv = tid / kWave, lane = tid % kWave;
+    const int b = blockIdx.x;
+    const int64_t nseg = (TK + kSegSlots - 1) / kSegSlots;
+    const int64_t seg = (int64_t)b * kRouteWaves + wv;
+    const int64_t f0 = seg * kSegSlots;
+
+    // the wave's slots (indices and weights, all loads at once), and this
+    // block's own segments counted again (one histogram per wave)
+    constexpr int kIt = kSegSlots / kWave;
+    int sl_e[kIt];
+    float sl_w[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+        const int64_t f = f0 + it * kWave + lane;
+        sl_e[it] = -1;
+        sl_w[it] = 0.f;
+        if (seg < nseg && f < TK) {
+            const int64_t v = topk_idx[f];
+            if (v >= 0 && v < E) {
+                sl_e[it] = (int)v;
+                sl_w[it] = topk_w[f];
+            }
+        }
+    }
+    int32_t* h = s_run + wv * E;
+    for (int e = lane; e < E; e += kWave) h[e] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < kIt; ++it)
+        if (sl_e[it] >= 0) atomicAdd(&h[sl_e[it]], 1);
+
+    // expert totals and rows in earlier blocks: P threads per expert, each
+    // summing a run of the blocks' histograms
+    int P = 1;
+    while (2 * P * E <= kRouteThreads) P *= 2;
+    for (int x = tid; x < P * E; x += kRouteThreads) {
+        const int e = x % E, p = x / E;
+        const int C = (nblk + P - 1) / P;
+        const int b0 = min(nblk, p * C), b1 = min(nblk, b0 + C);
+        int tot = 0, pre = 0;
+#pragma unroll 8
+        for (int bb = b0; bb < b1; ++bb) {
+            const int v = blk_hist[(int64_t)bb * E + e];
+            tot += v;
+            pre += bb < b ? v : 0;
+        }
+        if (P == 1) {
+            s_tot[e] = tot;
+            s_pre[e] = pre;
+        } else {
+            s_part[0][x] = tot;
+            s_part[1][x] = pre;
+        }
+    }
+    __syncthreads();
+    if (P > 1)
+        for (int e = tid; e < E; e += kRouteThreads) {
+            int tot = 0, pre = 0;
+            for (int p = 0; p < P; ++p) {
+                tot += s_part[0][p * E + e];
+                pre += s_part[1][p * E + e];
+            }
+            s_tot[e] = tot;
+            s_pre[e] = pre;
+        }
+    __syncthreads();
+
+    // offsets (exclusive scan of the totals) and each expert's first slot in
+    // this block's row list (exclusive scan of the block's counts); thread
+    // tid owns experts [ept*tid, ept*tid + ept)
+    const int ept = (E + kRouteThreads - 1) / kRouteThreads;
+    int my_tot = 0, my_blk = 0;
+    for (int j = 0; j < ept; ++j) {
+        const int e = ept * tid + j;
+        if (e < E) {
+            my_tot += s_tot[e];
+            int c = 0;
+#pragma unroll
+            for (int w = 0; w < kRouteWaves; ++w) c += s_run[w * E + e];
+            my_blk += c;
+        }
+    }
+    int R = 0, nrows = 0;
+    int off = block_exclusive_scan(my_tot, &R, s_w);
+    int loc = block_exclusive_scan(my_blk, &nrows, s_w);
+    for (int j = 0; j < ept; ++j) {
+        const int e = ept * tid + j;
+        if (e < E) {
+            s_off[e] = off;
+            s_loc[e] = loc;
+            // running bases of the block's waves: the expert's offset, its rows
+            // in earlier blocks, then the earlier waves of this block
+            int run = off + s_pre[e];
+#pragma unroll
+            for (int w = 0; w < kRouteWaves; ++w) {
+                const int c = s_run[w * E + e];
+                s_run[w * E + e] = run;
+                run += c;
+            }
+            off += s_tot[e];
+            loc += run - (s_off[e] + s_pre[e]);  // the block's rows of expert e
+        }
+    }
+    if (tid == 0) s_nrows = nrows;
+    __syncthreads();
+
+    // the stable rank of every slot of the wave's segment
+    if (seg < nseg) {
+        int32_t* run = s_run + wv * E;
+        const unsigned long long lt_mask = (1ull << lane) - 1ull;
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int64_t f = f0 + it * kWave + lane;
+            if (f0 + it * kWave >= TK) break;  // wave-uniform
+            const int e = sl_e[it];
+            const float w = sl_w[it];
+            unsigned long long peers = __ballot(e >= 0);
+            for (int bt = 0; bt < nbits; ++bt) {
+                const int bit = (e >> bt) & 1;
+                const unsigned long long set = __ballot(bit);
+                peers &= bit ? set : ~set;
+            }
+            if (e >= 0) {
+                const int base = run[e];
+                const int r = base + __popcll(peers & lt_mask);
+                const int32_t t = (int32_t)(f / K);
+                pool_src[r] = (int32_t)f;
+                slot_to_pool[f] = r;
+                pool_w[r] = w;
+                if (pool_tok) pool_tok[r] = t;
+                // the row's place in the block's list: the block's rows of
+                // expert e are the pool rows [s_off + s_pre, ...) in order
+                s_rows[s_loc[e] + (r - s_off[e] - s_pre[e])] = make_int2(r, t);
+                if ((peers >> lane) == 1ull) run[e] = base + __popcll(peers);  // highest peer lane
+            } else if (f < TK) {
+                slot_to_pool[f] = -1;
+            }
+        }
+    }
+    __syncthreads();
+
+    // the A-scale words of the block's pool rows, rows in ascending order
+    // within each expert (consecutive threads write consecutive words)
+    if (pool_s) {
+        const int n = s_nrows;
+        for (int i = tid; i < n; i += kRouteThreads) {
+            const int2 rt = s_rows[i];
+            const int64_t r = rt.x, t = rt.y;
+            if ((W & 3) == 0) {
+                const uint4* src = reinterpret_cast<const uint4*>(tok_s + t * W);
+                for (int w4 = 0; w4 < W / 4; ++w4) {
+                    const uint4 v = src[w4];
+                    pool_s[(int64_t)(4 * w4 + 0) * cap + r] = v.x;
+                    pool_s[(int64_t)(4 * w4 + 1) * cap + r] = v.y;
+                    pool_s[(int64_t)(4 * w4 + 2) * cap + r] = v.z;
+                    pool_s[(int64_t)(4 * w4 + 3) * cap + r] = v.w;
+                }
+            } else {
+                for (int w = 0; w < W; ++w) pool_s[(int64_t)w * cap + r] = tok_s[t * W + w];
+            }
+        }
+    }
+
+    if (b == 0) {
+        // counts, offsets, the expert-major m-tile table, the error flag
+        int my_nt = 0;
+        for (int j = 0; j < ept; ++j) {
+            const int e = ept * tid + j;
+            if (e < E) my_nt += (s_tot[e] + kBM - 1) / kBM;
+        }
+        int ntot = 0;
+        int toff = block_exclusive_scan(my_nt, &ntot, s_w);
+        for (int j = 0; j < ept; ++j) {
+            const int e = ept * tid + j;
+            if (e >= E) continue;
+            const int cnt = s_tot[e], nt = (cnt + kBM - 1) / kBM;
+            counts[e] = cnt;
+            offsets[e] = s_off[e];
+            for (int i = 0; i < nt; ++i) {
+                MTile m;
+                m.expert = e;
+                m.row0 = s_off[e] + i * kBM;
+                m.nrows = min(kBM, cnt - i * kBM);
+                m.pad = 0;
+                mtiles[toff + i] = m;
+            }
+            toff += nt;
+        }
+        int err = 0;
+        for (int bb = tid; bb < nblk; bb += kRouteThreads) err |= blk_err[bb];
+        err = __syncthreads_or(err);
+        if (tid == 0) {
+            offsets[E] = R;
+            *num_mtiles = ntot;
+            *err_flag = err ? 1 : 0;
+        }
+    }
+}
+
 // a4: gather + quantise.  A block takes tpb consecutive token rows (as many
 // as fit 8192 columns, else one) as one flat span; each lane owns 8
 // consecutive columns of up to four 2048-column chunks, whose 16-byte loads
@@ -297,18 +567,22 @@ __global__ __launch_bounds__(256) void k_dispatch_fp8(const uint16_t* __restrict
 }
 
 // The fused layer's first launch: blocks [0, ncount) compute the a1
-// per-segment histograms, the others quantise the token rows token-major
-// (the two are independent, so the histogram hides behind the row stream).
+// histograms (per segment, or with blk_hist set one per block of
+// kRouteWaves segments, for k_route), the others quantise the token rows
+// token-major (the two are independent, so the histogram hides behind the
+// row stream).
 __global__ __launch_bounds__(256) void k_quantise_count(const uint16_t* __restrict__ x, int64_t T,
                                                        int H, int tpb, uint8_t* __restrict__ x_q,
                                                        uint8_t* __restrict__ tok_s,
                                                        const int64_t* __restrict__ topk_idx,
                                                        int64_t TK, int E, int ncount,
                                                        int32_t* __restrict__ seg_hist,
-                                                       int32_t* __restrict__ seg_err) {
+                                                       int32_t* __restrict__ seg_err,
+                                                       int32_t* __restrict__ blk_hist,
+                                                       int32_t* __restrict__ blk_err) {
     extern __shared__ int32_t lds_hist[];  // [kRouteWaves][E]
     if ((int)blockIdx.x < ncount)
-        route_count_block(topk_idx, TK, E, seg_hist, seg_err, blockIdx.x, lds_hist);
+        route_count_block(topk_idx, TK, E, seg_hist, seg_err, blockIdx.x, lds_hist, blk_hist, blk_err);
     else
         dispatch_fp8_block(x, T, H, 1, tpb, nullptr, x_q, nullptr, tok_s, blockIdx.x - ncount);
 }
