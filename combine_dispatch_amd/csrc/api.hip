@@ -21,7 +21,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
     size_t seg_hist, seg_base, seg_err, blk_hist, blk_err, counts, offsets, mtiles, num_mtiles,
-        err_flag;
+        err_flag, mtiles64, num_mtiles64;
     size_t pool_src, slot_to_pool, pool_w, pool_tok, x_q, pool_s, act_q, act_s, l2_out, s1t, s2t,
         tok_s;
     size_t routing_end;  // bytes moe_dispatch needs
@@ -29,6 +29,7 @@ struct Layout {
     int64_t cap;         // pool rows incl. tile padding
     int64_t nseg;
     int64_t max_mtiles;
+    int64_t max_mtiles64;  // tiles of at most kDecRows rows
 };
 
 bool shape_basic_ok(const moe_shape_t* s) {
@@ -68,6 +69,9 @@ Layout make_layout(const moe_shape_t* s) {
     L.mtiles = take(sizeof(MTile) * L.max_mtiles);
     L.num_mtiles = take(sizeof(int32_t));
     L.err_flag = take(sizeof(int32_t));
+    L.max_mtiles64 = TK / kDecRows + (E < TK ? E : TK) + 1;
+    L.mtiles64 = take(sizeof(MTile) * L.max_mtiles64);
+    L.num_mtiles64 = take(sizeof(int32_t));
     L.routing_end = o;
     L.counts = take(sizeof(int32_t) * E);
     L.offsets = take(sizeof(int32_t) * (E + 1));
@@ -208,7 +212,8 @@ int run_routing(const moe_shape_t* s, const Layout& L, const int64_t* topk_idx, 
                            reinterpret_cast<int32_t*>(ws + L.num_mtiles),
                            reinterpret_cast<int32_t*>(ws + L.err_flag), pool_src, slot_to_pool, pool_w,
                            pool_tok, tok_s, s->H / 128, (int64_t)L.cap,
-                           static_cast<uint32_t*>(nullptr));
+                           static_cast<uint32_t*>(nullptr), reinterpret_cast<MTile*>(ws + L.mtiles64),
+                           reinterpret_cast<int32_t*>(ws + L.num_mtiles64));
         prof_mark(pc, MOE_STAGE_ROUTE_SCAN, stream);
         prof_mark(pc, MOE_STAGE_ROUTE_SCATTER, stream);
         // the scale words are a grid-wide copy (megabytes): a kernel of their own
@@ -401,9 +406,17 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
                            reinterpret_cast<int32_t*>(ws + L.blk_err));
     }
     prof_mark(pc, MOE_STAGE_DISPATCH, stream);
+    // few rows per expert (e.g. a decode batch): the decode-shaped GEMMs over
+    // the 64-row tile table that the one-launch routing writes.  For the
+    // smallest calls their L1 reads the A-scale words by token instead of a
+    // pool copy (a launch saved; measured: worth it at 128 routed rows, not
+    // at 1024, where the scattered reads cost the L1 GEMM as much)
+    const bool decode = route_fused(L, s->E) && (int64_t)T * K <= (int64_t)kDecRows * s->E;
+    const bool sa_by_token = decode && (int64_t)T * K <= 256;
     int rc = run_routing(s, L, topk_idx, topk_w, ws, pool_tok, counts, offsets, pool_src,
                          slot_to_pool, pool_w, stream, true, pc,
-                         reinterpret_cast<const uint32_t*>(tok_s), reinterpret_cast<uint32_t*>(pool_s));
+                         reinterpret_cast<const uint32_t*>(tok_s),
+                         sa_by_token ? static_cast<uint32_t*>(nullptr) : reinterpret_cast<uint32_t*>(pool_s));
     if (rc) return rc;
     if (o.debug_validate && (rc = check_routing_flag(ws, L, stream))) return rc;
 
@@ -427,14 +440,27 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     g1.act_s = act_s;
     g1.I = I;
     g1.fast_math = o.fast_math ? 1 : 0;
-    hipLaunchKernelGGL(k_gemm_l1, dim3(gemm_grid(L.max_mtiles * g1.ntiles)), dim3(kGemmThreads), 0,
-                       stream, g1);
+    if (decode) {
+        if (sa_by_token) {
+            g1.SA = tok_s;  // token-major words [T][H/128]
+            g1.sa_step = 4;
+            g1.sa_by_token = 1;
+        }
+        g1.mtiles = reinterpret_cast<const MTile*>(ws + L.mtiles64);
+        g1.num_mtiles = reinterpret_cast<const int32_t*>(ws + L.num_mtiles64);
+        hipLaunchKernelGGL(k_gemm_l1_decode, dim3((unsigned)(L.max_mtiles64 * g1.ntiles)),
+                           dim3(kGemmThreads), 0, stream, g1);
+    } else {
+        hipLaunchKernelGGL(k_gemm_l1, dim3(gemm_grid(L.max_mtiles * g1.ntiles)), dim3(kGemmThreads), 0,
+                           stream, g1);
+    }
     prof_mark(pc, MOE_STAGE_GEMM_L1, stream);
 
     GemmArgs g2 = g1;
     g2.A = act_q;
     g2.SA = act_s;
     g2.sa_step = 4 * L.cap;  // packed k-major words of the pool rows
+    g2.sa_by_token = 0;
     g2.pool_tok = nullptr;
     g2.B = W2q;
     g2.SB = s2t;
@@ -442,8 +468,12 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     g2.N = H;
     g2.ntiles = H / kBN;
     g2.out = l2_out;
-    hipLaunchKernelGGL(k_gemm_l2, dim3(gemm_grid(L.max_mtiles * g2.ntiles)), dim3(kGemmThreads), 0,
-                       stream, g2);
+    if (decode)
+        hipLaunchKernelGGL(k_gemm_l2_decode, dim3((unsigned)(L.max_mtiles64 * g2.ntiles)),
+                           dim3(kGemmThreads), 0, stream, g2);
+    else
+        hipLaunchKernelGGL(k_gemm_l2, dim3(gemm_grid(L.max_mtiles * g2.ntiles)), dim3(kGemmThreads), 0,
+                           stream, g2);
     prof_mark(pc, MOE_STAGE_GEMM_L2, stream);
 
     {

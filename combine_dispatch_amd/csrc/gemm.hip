@@ -1138,6 +1138,249 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     wait_all_loads();
 }
 
+// ---- decode-shaped GEMMs -------------------------------------------------
+// For batches whose experts hold few rows (at most kDecRows on average, e.g.
+// 128 tokens x 8 slots over 32 experts): the weights stream through once and
+// the bytes each CU keeps in flight set the speed (the page "Normal vs
+// Low-Latency", sections 5 and 10, names such a low-latency mode with a
+// shallower pipeline).  Here: tiles of at most 64 rows x 256 columns, one
+// workgroup per (tile, n-tile) -- no persistence, no cross-tile seam -- and
+// three LDS stages of 26 KB, so two workgroups share a CU and each keeps two
+// K steps of loads in flight while it multiplies the third.  The waves split
+// the columns as the narrow tiles of the persistent kernel do (b_row_narrow:
+// wave w has gate and up of quantisation group w in L1, column pairs in
+// L2), each covering rows 0-63 (two 32-row MFMA tiles): the same MFMAs in
+// the same K order for every output as there, hence the same results.
+// Loads per wave and K step: 2 A chunks of 1 KB, 4 B chunks of 1 KB, the
+// 64 rows' A-scale words (into the wave's own copy) and 64 of the 256 B-scale
+// words, all direct global->LDS.  With sa_by_token, L1 takes its rows'
+// A-scale words from the token-major words by token (GemmArgs SA = those
+// words, sa_step = 4), so the call needs no pool copy of them; as those are
+// 64 scattered words, wave 0 alone fetches them into a copy all waves read.
+template <int MODE>
+__device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, float* s_w) {
+    const int tid = threadIdx.x;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int tile = (int)blockIdx.x / g.ntiles;
+    const int nt = (int)blockIdx.x - tile * g.ntiles;
+    if (tile >= *g.num_mtiles) return;
+    const MTile rec = g.mtiles[tile];
+    const int e = __builtin_amdgcn_readfirstlane(rec.expert);
+    const int row0 = __builtin_amdgcn_readfirstlane(rec.row0);
+    const int nrows = __builtin_amdgcn_readfirstlane(rec.nrows);
+    const int Kdim = g.Kdim, nk = Kdim / kBK, b_ld = Kdim / 2;
+
+    // per-lane load offsets
+    // A: chunk q = tid + 256 i (i = 0, 1) is LDS row q/8, physical chunk q%8
+    // holding logical chunk (q%8) ^ ((row/2)%8); L1 rows come from the
+    // token-major codes through pool_tok (indices clamped into the buffer).
+    uint32_t a_off0, a_off1;
+    {
+        const uint32_t tmax = (uint32_t)(g.T - 1);
+        auto aoff = [&](int i) {
+            const int row = (tid >> 3) + 32 * i;
+            const int lch = (tid & 7) ^ ((row >> 1) & 7);
+            const uint32_t arow = MODE == kL1 ? min((uint32_t)g.pool_tok[row0 + row], tmax) : (uint32_t)row;
+            return arow * (uint32_t)Kdim + 16u * (uint32_t)lch;
+        };
+        a_off0 = aoff(0);
+        a_off1 = aoff(1);
+    }
+    // B: chunk q = tid + 256 i (i = 0..3) is LDS row q/4 (weight row
+    // b_row_narrow of it), physical chunk q%4 holding logical (q%4) ^ ((row/4)%4)
+    const int brow0 = b_row_narrow<MODE>(nt, 0, g.I);
+    auto boff = [&](int i) {
+        const int row = (tid >> 2) + 64 * i;
+        const int lch = (tid & 3) ^ ((row >> 2) & 3);
+        return (uint32_t)((b_row_narrow<MODE>(nt, row, g.I) - brow0) * b_ld + 16 * lch);
+    };
+    const uint32_t b_off0 = boff(0), b_off1 = boff(1), b_off2 = boff(2), b_off3 = boff(3);
+    // scale words: A row row0 + lane into the wave's copy -- L1 straight from
+    // the token-major words of its token (no pool copy of them), L2 from the
+    // packed k-major words of the pool rows; B: LDS word tid is the word of
+    // LDS B row tid
+    const bool sa_tok = MODE == kL1 && g.sa_by_token;
+    uint32_t sa_off;
+    if (sa_tok)
+        sa_off = 4u * min((uint32_t)g.pool_tok[row0 + lane], (uint32_t)(g.T - 1)) * (uint32_t)nk;
+    else
+        sa_off = 4u * (uint32_t)lane;
+    const uint32_t sb_off = (uint32_t)(4 * (b_row_narrow<MODE>(nt, tid, g.I) - brow0));
+    const uint8_t* a_base = MODE == kL1 ? g.A : g.A + (int64_t)row0 * Kdim;
+    const uint8_t* b_base = g.B + ((int64_t)e * g.N + brow0) * b_ld;
+    const uint8_t* sa_base = sa_tok ? g.SA : g.SA + (int64_t)row0 * 4;  // by token: token-major words
+    const int64_t sb_step = (int64_t)g.N * 4;
+    const uint8_t* sb_base = g.SB + (int64_t)e * nk * sb_step + (int64_t)brow0 * 4;
+
+    if (MODE == kL1 && tid < kDecRows) s_w[tid] = g.pool_w[row0 + tid];  // rows past the tile: unused
+
+    auto stage = [&](int k) { return lds + (k % kDecStages) * kDecStageBytes; };
+    auto issue = [&](int k) __attribute__((always_inline)) {
+        const uint32_t st = lds_addr(stage(k));
+        const uint32_t wa = st + 1024u * wid;
+        dma_x4(wa, a_base + k * kBK, a_off0);
+        dma_x4(wa + 4096, a_base + k * kBK, a_off1);
+        const uint32_t wb = st + kDecStageA + 1024u * wid;
+        dma_x4(wb, b_base + k * (kBK / 2), b_off0);
+        dma_x4(wb + 4096, b_base + k * (kBK / 2), b_off1);
+        dma_x4(wb + 8192, b_base + k * (kBK / 2), b_off2);
+        dma_x4(wb + 12288, b_base + k * (kBK / 2), b_off3);
+        if (sa_tok) {
+            // the rows' words scattered by token: wave 0 fetches them into
+            // the shared copy; the other waves keep the per-wave count of
+            // loads with a contiguous stand-in (the B words again) into
+            // their own unused slot
+            if (wid == 0)
+                dma_x1(st + kDecStageA + kDecStageB, sa_base + k * g.sa_step, sa_off);
+            else
+                dma_x1(st + kDecStageA + kDecStageB + 256u * wid, sb_base + k * sb_step, sb_off);
+        } else {
+            dma_x1(st + kDecStageA + kDecStageB + 256u * wid, sa_base + k * g.sa_step, sa_off);
+        }
+        dma_x1(st + kDecStageA + kDecStageB + kDecStageSA + 256u * wid, sb_base + k * sb_step, sb_off);
+    };
+
+    // this wave's column tiles (b_row_narrow): L1 gate and up of group wid,
+    // L2 the column pair 2 wid, 2 wid + 1
+    const int jn0 = MODE == kL1 ? wid : 2 * wid;
+    const int jn1 = MODE == kL1 ? wid + 4 : 2 * wid + 1;
+    const int a_sw = (l32 >> 1) & 7, b_sw = (l32 >> 2) & 3;
+    const int hs = 16 * h;
+    v16f acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    constexpr int kAhead = kDecStages - 1;  // K steps whose loads are in flight
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k)
+        if (k < nk) issue(k);
+    for (int k = 0; k < nk; ++k) {
+        // step k's loads have landed (the later steps' may still fly: 8
+        // loads per step and wave), and every wave is done reading step
+        // k-1's stage, which step k + kAhead then refills
+        const int later = min(kAhead - 1, nk - 1 - k);
+        if (later >= 3)
+            asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else if (later == 2)
+            asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else if (later == 1)
+            asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (k + kAhead < nk) issue(k + kAhead);
+        const uint8_t* sA = stage(k);
+        const uint8_t* sB = sA + kDecStageA;
+        const uint8_t* sSA = sB + kDecStageB + (sa_tok ? 0 : 256 * wid);  // by token: wave 0's copy
+        const uint8_t* sSB = sB + kDecStageB + kDecStageSA;
+        int wa0 = *reinterpret_cast<const int*>(sSA + 4 * l32);
+        int wa1 = *reinterpret_cast<const int*>(sSA + 4 * (32 + l32));
+        int wb0 = *reinterpret_cast<const int*>(sSB + 4 * (32 * jn0 + l32));
+        int wb1 = *reinterpret_cast<const int*>(sSB + 4 * (32 * jn1 + l32));
+        wa0 = (int)((uint32_t)wa0 >> hs);
+        wa1 = (int)((uint32_t)wa1 >> hs);
+        wb0 = (int)((uint32_t)wb0 >> hs);
+        wb1 = (int)((uint32_t)wb1 >> hs);
+        auto sub = [&](auto sconst) __attribute__((always_inline)) {
+            constexpr int S = decltype(sconst)::value;
+            v8i a[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint8_t* rowp = sA + (32 * i + l32) * kBK;
+                const uint4 v0 = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * S + h) ^ a_sw));
+                const uint4 v1 = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * S + 2 + h) ^ a_sw));
+                a[i] = v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+            }
+            v8i b[2];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const uint8_t* rowp = sB + (32 * (jj ? jn1 : jn0) + l32) * (kBK / 2);
+                const uint4 v = *reinterpret_cast<const uint4*>(rowp + 16 * ((2 * S + h) ^ b_sw));
+                b[jj] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        a[i], b[jj], acc[i][jj], 0, 4, S, i ? wa1 : wa0, S, jj ? wb1 : wb0);
+        };
+        sub(std::integral_constant<int, 0>{});
+        sub(std::integral_constant<int, 1>{});
+    }
+    wait_all_loads();
+
+    // epilogue (as for the narrow tiles of the persistent kernel): rows past
+    // the tile's end are dropped by the buffer range
+    if (MODE == kL2) {
+        const int N = g.N;
+        uint8_t* out_base = reinterpret_cast<uint8_t*>(g.out + (int64_t)row0 * N + nt * kBN);
+        const __amdgpu_buffer_rsrc_t out_rs = rows_rsrc(out_base, nrows * N * 2);
+        const int col = 64 * wid + 2 * l32;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lrow = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(acc[i][0][r], acc[i][1][r]), out_rs,
+                                                      2 * (lrow * N + col), 0, kStoreNT);
+            }
+        }
+    } else {
+        const int I = g.I;
+        uint8_t* q_base = g.act_q + (int64_t)row0 * I + nt * 128 + 32 * wid;
+        uint8_t* s_base = g.act_s + (int64_t)nt * g.act_s_step + (int64_t)row0 * 4;
+        const __amdgpu_buffer_rsrc_t q_rs = rows_rsrc(q_base, nrows * I);
+        const __amdgpu_buffer_rsrc_t s_rs = rows_rsrc(s_base, nrows * 4);
+        const int gbyte = ((wid & 1) << 1) | (wid >> 1);  // group wid in the word's byte order
+        const uint32_t bshift = 8u * (uint32_t)(l32 & 3);
+        __syncthreads();  // s_w visible
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int lrow0 = 32 * i + 8 * rq + 4 * h;
+                float gt[4], up[4], a[4];
+                uint32_t m[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const uint32_t gu = pack_bf16x2(acc[i][0][4 * rq + rr], acc[i][1][4 * rq + rr]);
+                    gt[rr] = bf16_lo(gu);
+                    up[rr] = bf16_hi(gu);
+                }
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const float wr = s_w[lrow0 + rr];
+                    if (g.fast_math) {
+                        const float ex = __builtin_amdgcn_exp2f(-gt[rr] * 1.4426950408889634f);
+                        a[rr] = ((gt[rr] * __builtin_amdgcn_rcpf(1.0f + ex)) * up[rr]) * wr;
+                    } else {
+                        a[rr] = ((gt[rr] / (1.0f + expf(-gt[rr]))) * up[rr]) * wr;
+                    }
+                    m[rr] = __float_as_uint(fabsf(a[rr]));
+                }
+                group32_max_u32x4(m);
+                uint32_t b[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    b[rr] = ue8m0_e4m3_bits(m[rr]);
+                    const uint32_t code = pack_fp8x2_scaled(a[rr], 0.f, b[rr]);
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code, q_rs, (lrow0 + rr) * I + l32, 0, kStoreNT);
+                }
+                // lanes l32 = 0..3 store the scale byte of rows lrow0 + l32
+                const uint32_t b4 = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+                const int s_off = l32 < 4 ? (lrow0 + l32) * 4 + gbyte : 0x40000000;
+                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(b4 >> bshift), s_rs, s_off, 0, 0);
+            }
+        }
+    }
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_l1(GemmArgs args) {
@@ -1156,6 +1399,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_l2(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) uint8_t st2[kStageBytes];
     __shared__ MTile s_tiles[kTileCache];
     gemm_persistent<kL2>(args, st0, st1, st2, nullptr, nullptr, s_tiles, nullptr);
+}
+
+
+__global__ __launch_bounds__(kGemmThreads, kDecWorkgroupsPerCU) void k_gemm_l1_decode(GemmArgs args) {
+    __shared__ __attribute__((aligned(16))) uint8_t st[kDecStages * kDecStageBytes];
+    __shared__ float s_w[kDecRows];
+    gemm_decode<kL1>(args, st, s_w);
+}
+
+__global__ __launch_bounds__(kGemmThreads, kDecWorkgroupsPerCU) void k_gemm_l2_decode(GemmArgs args) {
+    __shared__ __attribute__((aligned(16))) uint8_t st[kDecStages * kDecStageBytes];
+    gemm_decode<kL2>(args, st, nullptr);
 }
 
 }  // namespace moe

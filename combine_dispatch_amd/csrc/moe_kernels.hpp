@@ -30,6 +30,18 @@ struct MTile {
     int32_t expert, row0, nrows, pad;
 };
 
+// Decode-shaped GEMMs (batches whose experts hold few rows): tiles of at most
+// kDecRows rows, one workgroup per tile and n-tile, kDecStages LDS stages of
+// kDecStageBytes (two workgroups fit one CU).
+constexpr int kDecRows = 64;
+constexpr int kDecStages = 3;
+constexpr int kDecWorkgroupsPerCU = 2;  // by LDS: kDecStages * kDecStageBytes each
+constexpr int kDecStageA = kDecRows * kBK;      // e4m3 rows
+constexpr int kDecStageB = kBN * kBK / 2;       // e2m1 rows
+constexpr int kDecStageSA = 4 * kDecRows * 4;   // each wave's copy of the 64 rows' scale words
+constexpr int kDecStageSB = kBN * 4;
+constexpr int kDecStageBytes = kDecStageA + kDecStageB + kDecStageSA + kDecStageSB;
+
 // Tile records a persistent GEMM workgroup keeps in LDS: the launch must give
 // no workgroup more tiles than this (at most ceil(ceil(tiles / 8) / (grid / 8))).
 constexpr int kTileCache = 256;
@@ -60,6 +72,7 @@ struct GemmArgs {
     int64_t act_s_step;  // 4 * cap
     int32_t I;
     int32_t fast_math;
+    int32_t sa_by_token;  // decode L1: SA = token-major words [T][Kdim/128], read by pool_tok
     // L2 epilogue
     uint16_t* out;       // bf16 [rows][N]
 };
@@ -79,7 +92,8 @@ __global__ void k_route(const int64_t* __restrict__ topk_idx, const float* __res
                         int32_t* __restrict__ pool_src, int32_t* __restrict__ slot_to_pool,
                         float* __restrict__ pool_w, int32_t* __restrict__ pool_tok,
                         const uint32_t* __restrict__ tok_s, int W, int64_t cap,
-                        uint32_t* __restrict__ pool_s);
+                        uint32_t* __restrict__ pool_s, MTile* __restrict__ mtiles64,
+                        int32_t* __restrict__ num_mtiles64);
 __global__ void k_route_scan(const int32_t* __restrict__ seg_hist,
                              const int32_t* __restrict__ seg_err, int nseg, int E,
                              int32_t* __restrict__ seg_base, int32_t* __restrict__ counts,
@@ -120,5 +134,7 @@ __global__ void k_combine(const uint16_t* __restrict__ o, const int32_t* __restr
                           uint16_t* __restrict__ y);
 __global__ void k_gemm_l1(GemmArgs args);
 __global__ void k_gemm_l2(GemmArgs args);
+__global__ void k_gemm_l1_decode(GemmArgs args);
+__global__ void k_gemm_l2_decode(GemmArgs args);
 
 }  // namespace moe

@@ -266,7 +266,8 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int32_t* 
 // its pool rows from their tokens' words (tok_s, [T][W]) into the GEMM's
 // packed k-major layout (word (w, r) at w * cap + r), one thread per row in
 // the order of the rows.  Block 0 also writes counts, offsets, the GEMM's
-// expert-major m-tile table and the routing error flag.
+// expert-major m-tile table (and with mtiles64 set the same rows in tiles
+// of at most kDecRows rows) and the routing error flag.
 __global__ __launch_bounds__(kRouteThreads) void k_route(
     const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int64_t TK, int E,
     int nbits, int K, const int32_t* __restrict__ blk_hist, const int32_t* __restrict__ blk_err,
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
     MTile* __restrict__ mtiles, int32_t* __restrict__ num_mtiles, int32_t* __restrict__ err_flag,
     int32_t* __restrict__ pool_src, int32_t* __restrict__ slot_to_pool, float* __restrict__ pool_w,
     int32_t* __restrict__ pool_tok, const uint32_t* __restrict__ tok_s, int W, int64_t cap,
-    uint32_t* __restrict__ pool_s) {
+    uint32_t* __restrict__ pool_s, MTile* __restrict__ mtiles64, int32_t* __restrict__ num_mtiles64) {
     extern __shared__ int32_t lds[];
     int32_t* s_tot = lds;                     // [E] expert totals
     int32_t* s_pre = s_tot + E;               // [E] rows of the expert in blocks before this one
@@ -473,12 +474,37 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
             }
             toff += nt;
         }
+        // the same rows in 64-row tiles, for the decode-shaped GEMMs
+        int ntot64 = 0;
+        if (mtiles64) {
+            int my64 = 0;
+            for (int j = 0; j < ept; ++j) {
+                const int e = ept * tid + j;
+                if (e < E) my64 += (s_tot[e] + kDecRows - 1) / kDecRows;
+            }
+            int t64 = block_exclusive_scan(my64, &ntot64, s_w);
+            for (int j = 0; j < ept; ++j) {
+                const int e = ept * tid + j;
+                if (e >= E) continue;
+                const int cnt = s_tot[e], nt = (cnt + kDecRows - 1) / kDecRows;
+                for (int i = 0; i < nt; ++i) {
+                    MTile m;
+                    m.expert = e;
+                    m.row0 = s_off[e] + i * kDecRows;
+                    m.nrows = min(kDecRows, cnt - i * kDecRows);
+                    m.pad = 0;
+                    mtiles64[t64 + i] = m;
+                }
+                t64 += nt;
+            }
+        }
         int err = 0;
         for (int bb = tid; bb < nblk; bb += kRouteThreads) err |= blk_err[bb];
         err = __syncthreads_or(err);
         if (tid == 0) {
             offsets[E] = R;
             *num_mtiles = ntot;
+            if (num_mtiles64) *num_mtiles64 = ntot64;
             *err_flag = err ? 1 : 0;
         }
     }

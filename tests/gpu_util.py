@@ -69,3 +69,11 @@ def view(workspace: torch.Tensor, inp: dict, name: str, rows: int | None = None)
         shape = (rows,) + shape[1:]
     nbytes = int(np.prod(shape)) * np.dtype(dt).itemsize
     return workspace[off:off + nbytes].cpu().numpy().view(dt).reshape(shape)
+
+
+def uses_decode_path(inp: dict) -> bool:
+    """Whether the fused layer leaves the workspace's pool_s unwritten: its
+    decode-shaped GEMMs (at most 64 routed rows per expert on average) read
+    the A-scale words by token when there are at most 256 routed rows."""
+    TK = inp["T"] * inp["K"]
+    return TK <= 64 * inp["E"] and TK <= 256
