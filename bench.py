@@ -15,12 +15,15 @@ times that path instead.
 Prints ONE JSON line (rank 0):
   value        whole-layer TFLOP/s = 6*R*H*I / step time (R = routed rows)
   routed_rows_per_s
-  roofline     the dominant kernel (the L1 GEMM): algorithmic FLOP per launch
-               / its average duration from HIP events on its stream (recorded
-               by the library around each launch over a second run of the
-               same number of steps; the first, timed run has none), against
-               the FP8 dense MFMA peak (the FP8 x FP4 scaled MFMA runs at the
-               FP8 rate)
+  roofline     the dominant kernel (the L1 GEMM), its average duration from
+               HIP events on its stream (recorded by the library around each
+               launch over a second run of the same number of steps; the
+               first, timed run has none), against whichever bound its
+               algorithmic work meets first: FLOP per launch against the FP8
+               dense MFMA peak (the FP8 x FP4 scaled MFMA runs at the FP8
+               rate), or algorithmic bytes per launch (experts' W1 and its
+               scales once, token codes once, routed rows' A-scale words,
+               activations written) against HBM bandwidth
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -68,9 +71,13 @@ def parse():
 # that leave the L2 for the fabric -- Infinity Cache hits included -- plus
 # writes), from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) scaled by
 # a plain copy of known size.  This is an upper bound on its HBM bytes, not
-# HBM bytes themselves.  The summary names the sha256 of the GEMM sources it
-# was measured on; a changed kernel reports null.
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_l1_prefill_hbm_traffic.md")
+# HBM bytes themselves.  One summary per workload; each names the sha256 of
+# the GEMM sources it was measured on, and a changed kernel reports null.
+def traffic_summary(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"gemm_l1_{workload}_hbm_traffic.md")
+
+
+
 GEMM_SOURCES = ("combine_dispatch_amd/csrc/gemm.hip", "combine_dispatch_amd/csrc/moe_kernels.hpp",
                 "combine_dispatch_amd/csrc/moe_device.hpp")
 
@@ -85,10 +92,11 @@ def gemm_source_hash() -> str:
 
 
 def measured_traffic(workload: str):
-    if workload != "prefill" or not os.path.exists(TRAFFIC_SUMMARY):
+    path = traffic_summary(workload)
+    if not os.path.exists(path):
         return None
     fields = {}
-    for line in open(TRAFFIC_SUMMARY):
+    for line in open(path):
         m = re.match(r"^\s*-?\s*`?([a-z0-9_]+)`?\s*:\s*`?([0-9a-f.]+)`?\s*$", line)
         if m:
             fields[m.group(1)] = m.group(2)
@@ -255,7 +263,19 @@ def main():
     rows_s = R / (ms_per_step * 1e-3)
     l1_flop = 4.0 * R * H * I
     l2_flop = 2.0 * R * I * H
-    l1_tflops = l1_flop / (per_launch["gemm_l1"] * 1e-3) / 1e12
+    l1_s = per_launch["gemm_l1"] * 1e-3
+    l1_tflops = l1_flop / l1_s / 1e12
+    # L1 algorithmic bytes: W1 codes and scales of every expert that holds a
+    # routed row, the token rows' codes once, each routed row's A-scale words,
+    # its weight and token index, the e4m3 activations and their scales
+    experts_used = int(np.unique(inp["topk_idx"][inp["topk_idx"] >= 0]).size)
+    l1_bytes = (experts_used * 2 * I * (H // 2 + H // 32) + T * H + R * (H // 32 + 8)
+                + R * (I + I // 32))
+    l1_bound = "mfma" if l1_flop / PEAK_TFLOPS >= l1_bytes / PEAK_HBM_GBS * 1e3 else "hbm"
+    l1_gbs = l1_bytes / l1_s / 1e9
+    # the library's GEMMs with 64-row tiles serve batches with at most 64
+    # routed slots per expert on average
+    l1_kernel = "gemm_l1_decode" if T * K <= 64 * E else "gemm_l1"
     l2_tflops = l2_flop / (per_launch["gemm_l2"] * 1e-3) / 1e12
     # algorithmic bytes of the bandwidth-bound kernels (see the design notes):
     # dispatch = x read, token-major codes and scale words written, topk_idx
@@ -266,6 +286,17 @@ def main():
     comb_bytes = R * H * 2 + T * H * 2 + T * K * 4
 
     traffic = measured_traffic(a.workload)
+    roofline = {"bound": l1_bound, "kernel": l1_kernel}
+    if l1_bound == "mfma":
+        roofline.update(achieved=round(l1_tflops, 2), peak=PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=round(l1_tflops / PEAK_TFLOPS, 4))
+    else:
+        roofline.update(achieved=round(l1_gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=round(l1_gbs / PEAK_HBM_GBS, 4))
+    roofline.update(traffic=traffic, algorithmic_flop_per_launch=l1_flop,
+                    algorithmic_bytes_per_launch=l1_bytes,
+                    traffic_kind="bytes across the XCD L2 boundary per launch (FETCH_SIZE x2 + "
+                                 "WRITE_SIZE, Infinity Cache hits included): an upper bound on HBM bytes")
 
     out = {
         "metric": METRIC,
@@ -289,12 +320,7 @@ def main():
                    "parallelism": "single GPU, all experts local"},
         "routed_rows_per_s": round(rows_s, 1),
         "frac_of_fp8_peak": round(tflops / PEAK_TFLOPS, 4),
-        "roofline": {"bound": "mfma", "kernel": "gemm_l1", "achieved": round(l1_tflops, 2),
-                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(l1_tflops / PEAK_TFLOPS, 4),
-                     "traffic": traffic,
-                     "traffic_kind": "bytes across the XCD L2 boundary per launch "
-                                     "(FETCH_SIZE x2 + WRITE_SIZE, Infinity Cache hits included): "
-                                     "an upper bound on HBM bytes"},
+        "roofline": roofline,
         "kernels_ms_per_launch": {k: round(v, 4) for k, v in per_launch.items()},
         "ms_per_step_with_kernel_events": round(ms_per_step_events, 4),
         "kernels": {

@@ -23,9 +23,13 @@ enum {
     MOE_STAGE_WEIGHT_SCALES = 0, /* weight scales -> packed k-major words (canonical entry only) */
     MOE_STAGE_DISPATCH,        /* a4: e4m3 quantisation of the token rows; a1 per-segment
                                   expert histogram in the same launch */
-    MOE_STAGE_ROUTE_SCAN,      /* a2: offsets, segment bases, m-tile table */
-    MOE_STAGE_ROUTE_SCATTER,   /* a3: stable rank -> pool_src, slot_to_pool, pool_w, pool_tok */
-    MOE_STAGE_POOL_SCALES,     /* a4: the pool rows' scale words gathered by token */
+    MOE_STAGE_ROUTE_SCAN,      /* a2: offsets, segment bases, m-tile tables; in the one-launch
+                                  routing (k_route) also a3 */
+    MOE_STAGE_ROUTE_SCATTER,   /* a3: stable rank -> pool_src, slot_to_pool, pool_w, pool_tok
+                                  (an empty interval when a3 ran in the one launch above) */
+    MOE_STAGE_POOL_SCALES,     /* a4: the pool rows' scale words gathered by token (empty when
+                                  the L1 GEMM reads them by token: at most 256 routed slots
+                                  and at most 64 per expert on average) */
     MOE_STAGE_GEMM_L1,         /* a5-a7: L1 GEMM (gathers the token rows), SwiGLU*w, e4m3 requant */
     MOE_STAGE_GEMM_L2,         /* a8: L2 GEMM, bf16 rows */
     MOE_STAGE_COMBINE,         /* a9: top-k fp32 reduction to bf16 */

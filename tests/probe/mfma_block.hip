@@ -63,3 +63,75 @@ extern "C" int mfma_block_run(const void* A, const void* B, const void* sa, cons
                        (const uint8_t*)sb, (float*)D);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
+
+// ---- throughput of the same MFMA with register-resident operands ----------
+// Every wave runs `iters` rounds of 8 independent accumulator chains
+// (v_mfma_scale_f32_32x32x64_f8f6f4, A format 0 = e4m3, B format fmt_b: 4 =
+// e2m1, 0 = e4m3), no memory traffic in the loop.  Operands: `random` = 0 ->
+// one constant byte pattern in every operand; 1 -> four pseudo-random operand
+// sets per lane, rotated between MFMAs so consecutive MFMAs see different
+// bits (as real data does).  One 256-thread workgroup per CU; out gets a
+// checksum so the loop is kept.
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+    x ^= x >> 16; x *= 0x7feb352dU; x ^= x >> 15; x *= 0x846ca68bU; x ^= x >> 16;
+    return x;
+}
+
+template <int FMT_B>
+__device__ __forceinline__ void mfma_rate_body(int iters, int random, float* out) {
+    const uint32_t lane = threadIdx.x + 256u * blockIdx.x;
+    v8i a[4], b[4];
+    for (int s = 0; s < 4; ++s)
+        for (int r = 0; r < 8; ++r) {
+            const uint32_t ra = random ? mix32(lane * 64u + 16u * s + r) : 0x3C3C3C3Cu;
+            const uint32_t rb = random ? mix32(0x9e3779b9u ^ (lane * 64u + 16u * s + r)) : 0x3C3C3C3Cu;
+            // e4m3: avoid the NaN codes 0x7F / 0xFF
+            a[s][r] = (int)(ra & 0xF7F7F7F7u);
+            b[s][r] = (int)(FMT_B == 0 ? (rb & 0xF7F7F7F7u) : rb);
+            if (FMT_B == 4 && r >= 4) b[s][r] = 0;  // e2m1 uses 4 registers
+        }
+    v16f acc[8];
+    for (int j = 0; j < 8; ++j)
+        for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+    // rounds in groups of 4 so every operand index is a compile-time constant
+    for (int it = 0; it < iters; it += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[j & 3], b[(j + u) & 3], acc[j], 0,
+                                                                          FMT_B, 0, 127, 0, 127);
+    }
+    float s = 0.f;
+    for (int j = 0; j < 8; ++j)
+        for (int r = 0; r < 16; ++r) s += acc[j][r];
+    out[lane] = s;
+}
+
+__global__ __launch_bounds__(256, 1) void k_mfma_rate_fp4(int iters, int random, float* out) {
+    mfma_rate_body<4>(iters, random, out);
+}
+__global__ __launch_bounds__(256, 1) void k_mfma_rate_fp8(int iters, int random, float* out) {
+    mfma_rate_body<0>(iters, random, out);
+}
+
+// Runs the loop (iters rounded up to a multiple of 4) on `blocks` workgroups; B format 4 (e2m1) or 0 (e4m3).
+// Returns the elapsed milliseconds from HIP events (or a negative value on
+// a failed launch).  out must hold blocks * 256 floats.
+extern "C" float mfma_rate_run(int fmt_b, int random, int iters, int blocks, void* out) {
+    if (blocks < 1 || iters < 1 || !out || (fmt_b != 0 && fmt_b != 4)) return -1.f;
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -2.f;
+    hipEventRecord(e0, nullptr);
+    if (fmt_b == 4)
+        hipLaunchKernelGGL(k_mfma_rate_fp4, dim3(blocks), dim3(256), 0, nullptr, iters, random, (float*)out);
+    else
+        hipLaunchKernelGGL(k_mfma_rate_fp8, dim3(blocks), dim3(256), 0, nullptr, iters, random, (float*)out);
+    hipEventRecord(e1, nullptr);
+    float ms = -3.f;
+    if (hipGetLastError() == hipSuccess && hipEventSynchronize(e1) == hipSuccess)
+        hipEventElapsedTime(&ms, e0, e1);
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    return ms;
+}
