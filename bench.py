@@ -61,6 +61,9 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="also capture one moe_fused_forward_packed step into a HIP graph and report the replayed step "
                         "time (ms_per_step_graph) beside the main number")
+    p.add_argument("--gemm-tiles", choices=("auto", "persistent", "64", "128"), default="auto",
+                   help="which grouped-GEMM kernels the layer runs (moe_options_t.gemm_tiles); "
+                        "auto: the library's choice by shape")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="after the timed region, run one plain device-to-device copy of this "
                         "many MiB (the known-size kernel that scales the HBM byte counters)")
@@ -146,13 +149,16 @@ def main():
     packed = torch.empty(moe.moe_packed_scales_bytes(H, I, E), dtype=torch.uint8, device=dev)
     moe.moe_pack_weight_scales(d["S1"], d["S2"], packed, E=E, H=H, I=I, stream=stream)
 
+    opts = moe.options(gemm_tiles={"auto": moe.MOE_TILES_AUTO, "persistent": moe.MOE_TILES_PERSISTENT,
+                                   "64": moe.MOE_TILES_64, "128": moe.MOE_TILES_128}[a.gemm_tiles])
+
     def step_packed():
         moe.moe_fused_forward_packed(d["x"], d["topk_idx"], d["topk_w"], d["W1q"], d["W2q"],
-                                     packed, y, ws, E=E, I=I, stream=stream)
+                                     packed, y, ws, opts=opts, E=E, I=I, stream=stream)
 
     def step_canonical():
         moe.moe_fused_forward(d["x"], d["topk_idx"], d["topk_w"], d["W1q"], d["S1"], d["W2q"],
-                              d["S2"], y, ws, E=E, I=I, stream=stream)
+                              d["S2"], y, ws, opts=opts, E=E, I=I, stream=stream)
 
     step, other = ((step_packed, step_canonical) if a.scales == "packed"
                    else (step_canonical, step_packed))
@@ -229,13 +235,13 @@ def main():
         cap.wait_stream(stream)
         with torch.cuda.stream(cap):
             moe.moe_fused_forward_packed(d["x"], d["topk_idx"], d["topk_w"], d["W1q"], d["W2q"],
-                                         packed, y, ws, E=E, I=I, stream=cap)
+                                         packed, y, ws, opts=opts, E=E, I=I, stream=cap)
         stream.wait_stream(cap)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             moe.moe_fused_forward_packed(d["x"], d["topk_idx"], d["topk_w"], d["W1q"], d["W2q"],
-                                         packed, y, ws, E=E, I=I,
+                                         packed, y, ws, opts=opts, E=E, I=I,
                                          stream=torch.cuda.current_stream())
         for _ in range(3):
             graph.replay()
@@ -275,7 +281,8 @@ def main():
     l1_gbs = l1_bytes / l1_s / 1e9
     # the library's GEMMs with 64-row tiles serve batches with at most 64
     # routed slots per expert on average
-    l1_kernel = "gemm_l1_decode" if T * K <= 64 * E else "gemm_l1"
+    l1_kernel = {"64": "gemm_l1_decode", "128": "gemm_l1_t128", "persistent": "gemm_l1"}.get(
+        a.gemm_tiles, "gemm_l1_decode" if T * K <= 64 * E else "gemm_l1")
     l2_tflops = l2_flop / (per_launch["gemm_l2"] * 1e-3) / 1e12
     # algorithmic bytes of the bandwidth-bound kernels (see the design notes):
     # dispatch = x read, token-major codes and scale words written, topk_idx
@@ -317,7 +324,7 @@ def main():
                    "T": T, "H": H, "I": I, "E": E, "K": K, "routed_rows": R,
                    "weight_scales": ("packed once before timing (moe_pack_weight_scales)"
                                      if a.scales == "packed" else "re-laid every step"),
-                   "parallelism": "single GPU, all experts local"},
+                   "parallelism": "single GPU, all experts local", "gemm_tiles": a.gemm_tiles},
         "routed_rows_per_s": round(rows_s, 1),
         "frac_of_fp8_peak": round(tflops / PEAK_TFLOPS, 4),
         "roofline": roofline,

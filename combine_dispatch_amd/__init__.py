@@ -29,6 +29,10 @@ MOE_ERR_TOO_LARGE = -6
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_PAYLOAD_FP8_E4M3 = 0
 MOE_PAYLOAD_BF16 = 1
+MOE_TILES_AUTO = 0
+MOE_TILES_PERSISTENT = 1
+MOE_TILES_64 = 2
+MOE_TILES_128 = 3
 
 EXPORTED = ("moe_default_options", "moe_workspace_bytes", "moe_dispatch_workspace_bytes",
             "moe_fused_forward", "moe_dispatch", "moe_combine", "moe_workspace_views",
@@ -45,7 +49,7 @@ class MoeShape(ctypes.Structure):
 
 class MoeOptions(ctypes.Structure):
     _fields_ = [("fast_math", ctypes.c_int32), ("activation_clamp", ctypes.c_float),
-                ("debug_validate", ctypes.c_int32)]
+                ("debug_validate", ctypes.c_int32), ("gemm_tiles", ctypes.c_int32)]
 
 
 class MoeWorkspaceViews(ctypes.Structure):
@@ -134,10 +138,10 @@ def moe_default_options() -> MoeOptions:
 
 
 def options(fast_math: bool = True, activation_clamp: float | None = None,
-            debug_validate: bool = False) -> MoeOptions:
+            debug_validate: bool = False, gemm_tiles: int = MOE_TILES_AUTO) -> MoeOptions:
     return MoeOptions(1 if fast_math else 0,
                       math.nan if activation_clamp is None else float(activation_clamp),
-                      1 if debug_validate else 0)
+                      1 if debug_validate else 0, int(gemm_tiles))
 
 
 def moe_workspace_bytes(T: int, H: int, I: int, E: int, K: int) -> int:

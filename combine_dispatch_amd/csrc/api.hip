@@ -183,13 +183,33 @@ int route_blocks(const Layout& L) { return (int)((L.nseg + kRouteWaves - 1) / kR
 // block histograms; otherwise a single-block scan, then the scatter.
 bool route_fused(const Layout& L, int E) { return (int64_t)route_blocks(L) * E <= kRouteFusedMax; }
 
+// Which GEMM kernels a call runs.  rm = 0: both persistent over 256-row
+// tiles; rm = 1: both tile-per-workgroup over 64-row tiles (at most 64
+// routed slots per expert on average: the weights stream through once);
+// rm = 2: 128-row tiles for l1 / l2 where set.  The tile-per-workgroup
+// kernels read the second tile table, which the one-launch routing writes.
+struct TilePlan {
+    int rm;
+    bool l1, l2;
+};
+constexpr bool kT128L1 = false, kT128L2 = false;
+TilePlan tile_plan(const moe_shape_t* s, const Layout& L, int choice) {
+    const int64_t TK = (int64_t)s->T * s->K;
+    if (choice == MOE_TILES_PERSISTENT || !route_fused(L, s->E)) return {0, false, false};
+    if (choice == MOE_TILES_64) return {1, true, true};
+    if (choice == MOE_TILES_128) return {2, true, true};
+    if (TK <= (int64_t)kDecRows * s->E) return {1, true, true};
+    if (kT128L1 || kT128L2) return {2, kT128L1, kT128L2};
+    return {0, false, false};
+}
+
 // a1 (unless the caller's first launch already counted: `counted`), a2, a3,
 // and, with pool_s set, the pool rows' A-scale words gathered from the
 // token words tok_s ([T][W]) into the GEMM's packed k-major layout.
 int run_routing(const moe_shape_t* s, const Layout& L, const int64_t* topk_idx, const float* topk_w,
                 uint8_t* ws, int32_t* pool_tok, int32_t* counts, int32_t* offsets, int32_t* pool_src,
                 int32_t* slot_to_pool, float* pool_w, hipStream_t stream, bool counted, int pc,
-                const uint32_t* tok_s, uint32_t* pool_s) {
+                const uint32_t* tok_s, uint32_t* pool_s, int dec_rows = kDecRows) {
     const int64_t TK = (int64_t)s->T * s->K;
     const int E = s->E;
     const int nblk = route_blocks(L);
@@ -213,7 +233,7 @@ int run_routing(const moe_shape_t* s, const Layout& L, const int64_t* topk_idx, 
                            reinterpret_cast<int32_t*>(ws + L.err_flag), pool_src, slot_to_pool, pool_w,
                            pool_tok, tok_s, s->H / 128, (int64_t)L.cap,
                            static_cast<uint32_t*>(nullptr), reinterpret_cast<MTile*>(ws + L.mtiles64),
-                           reinterpret_cast<int32_t*>(ws + L.num_mtiles64));
+                           reinterpret_cast<int32_t*>(ws + L.num_mtiles64), dec_rows);
         prof_mark(pc, MOE_STAGE_ROUTE_SCAN, stream);
         prof_mark(pc, MOE_STAGE_ROUTE_SCATTER, stream);
         // the scale words are a grid-wide copy (megabytes): a kernel of their own
@@ -285,6 +305,7 @@ moe_options_t moe_default_options(void) {
     o.fast_math = 1;
     o.activation_clamp = NAN;
     o.debug_validate = 0;
+    o.gemm_tiles = MOE_TILES_AUTO;
     return o;
 }
 
@@ -352,6 +373,7 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     if (!shape_basic_ok(s)) return MOE_ERR_INVALID_ARG;
     const moe_options_t o = opt ? *opt : moe_default_options();
     if (!isnan(o.activation_clamp)) return MOE_ERR_UNSUPPORTED;
+    if (o.gemm_tiles < MOE_TILES_AUTO || o.gemm_tiles > MOE_TILES_128) return MOE_ERR_INVALID_ARG;
     if (!fused_shape_ok(s)) return MOE_ERR_UNSUPPORTED;
     if (s->T == 0) return MOE_OK;
     if (!x || !topk_idx || !topk_w || !W1q || !W2q || !y) return MOE_ERR_INVALID_ARG;
@@ -363,6 +385,8 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
             return MOE_ERR_INVALID_ARG;  // scale rows are read as 4-byte words
     }
     const Layout L = make_layout(s);
+    if ((o.gemm_tiles == MOE_TILES_64 || o.gemm_tiles == MOE_TILES_128) && !route_fused(L, s->E))
+        return MOE_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
         return MOE_ERR_WORKSPACE;
     if (!device_ok()) return MOE_ERR_DEVICE;
@@ -389,13 +413,43 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     if (!packed) launch_pack_scales(s, S1, S2, ws + L.s1t, ws + L.s2t, stream);
     prof_mark(pc, MOE_STAGE_WEIGHT_SCALES, stream);
     uint8_t* tok_s = ws + L.tok_s;
-    {
+    // few rows per expert (e.g. a decode batch): the decode-shaped GEMMs over
+    // the 64-row tile table that the one-launch routing writes.  For the
+    // smallest calls their L1 reads the A-scale words by token instead of a
+    // pool copy (a launch saved; measured: worth it at 128 routed rows, not
+    // at 1024, where the scattered reads cost the L1 GEMM as much)
+    const TilePlan plan = tile_plan(s, L, o.gemm_tiles);
+    const bool decode = plan.rm == 1;
+    const bool sa_by_token = decode && (int64_t)T * K <= 256;
+    const int drows = plan.rm ? dec_rows(plan.rm) : kDecRows;
+    const int tpb = tokens_per_block(H);
+    const int64_t nq = ((int64_t)T + tpb - 1) / tpb;
+    int rc = MOE_OK;
+    if ((int64_t)T * K <= kRouteSingleMax) {
+        // one launch for a1-a4: block 0 routes the whole batch while the
+        // others quantise the token rows
+        hipLaunchKernelGGL(k_quantise_route, dim3((unsigned)(1 + nq)), dim3(256), route_lds_bytes(s->E),
+                           stream, static_cast<const uint16_t*>(x), (int64_t)T, H, tpb, x_q, tok_s,
+                           topk_idx, topk_w, (int64_t)T * K, s->E, bits_for(s->E), K, counts, offsets,
+                           reinterpret_cast<MTile*>(ws + L.mtiles),
+                           reinterpret_cast<int32_t*>(ws + L.num_mtiles),
+                           reinterpret_cast<int32_t*>(ws + L.err_flag), pool_src, slot_to_pool, pool_w,
+                           pool_tok, reinterpret_cast<MTile*>(ws + L.mtiles64),
+                           reinterpret_cast<int32_t*>(ws + L.num_mtiles64), drows);
+        prof_mark(pc, MOE_STAGE_DISPATCH, stream);
+        prof_mark(pc, MOE_STAGE_ROUTE_SCAN, stream);
+        prof_mark(pc, MOE_STAGE_ROUTE_SCATTER, stream);
+        if (!sa_by_token)
+            hipLaunchKernelGGL(k_pool_scales, dim3((unsigned)((L.cap + 255) / 256)), dim3(256), 0, stream,
+                               reinterpret_cast<const uint32_t*>(tok_s), H / 128, pool_tok, offsets, s->E,
+                               (int64_t)L.cap, reinterpret_cast<uint32_t*>(pool_s));
+        prof_mark(pc, MOE_STAGE_POOL_SCALES, stream);
+        rc = launch_status();
+    } else {
         // every token row quantised once, token-major (the L1 GEMM gathers the
         // rows of its tiles through pool_tok); the a1 histogram in the same
         // launch
-        const int tpb = tokens_per_block(H);
         const int ncount = route_blocks(L);
-        const int64_t nq = ((int64_t)T + tpb - 1) / tpb;
         hipLaunchKernelGGL(k_quantise_count, dim3((unsigned)(ncount + nq)), dim3(256),
                            sizeof(int32_t) * kRouteWaves * s->E, stream,
                            static_cast<const uint16_t*>(x), (int64_t)T, H, tpb, x_q, tok_s, topk_idx,
@@ -404,21 +458,19 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
                            route_fused(L, s->E) ? reinterpret_cast<int32_t*>(ws + L.blk_hist)
                                                 : static_cast<int32_t*>(nullptr),
                            reinterpret_cast<int32_t*>(ws + L.blk_err));
+        prof_mark(pc, MOE_STAGE_DISPATCH, stream);
+        rc = run_routing(s, L, topk_idx, topk_w, ws, pool_tok, counts, offsets, pool_src, slot_to_pool,
+                         pool_w, stream, true, pc, reinterpret_cast<const uint32_t*>(tok_s),
+                         sa_by_token ? static_cast<uint32_t*>(nullptr) : reinterpret_cast<uint32_t*>(pool_s),
+                         drows);
     }
-    prof_mark(pc, MOE_STAGE_DISPATCH, stream);
-    // few rows per expert (e.g. a decode batch): the decode-shaped GEMMs over
-    // the 64-row tile table that the one-launch routing writes.  For the
-    // smallest calls their L1 reads the A-scale words by token instead of a
-    // pool copy (a launch saved; measured: worth it at 128 routed rows, not
-    // at 1024, where the scattered reads cost the L1 GEMM as much)
-    const bool decode = route_fused(L, s->E) && (int64_t)T * K <= (int64_t)kDecRows * s->E;
-    const bool sa_by_token = decode && (int64_t)T * K <= 256;
-    int rc = run_routing(s, L, topk_idx, topk_w, ws, pool_tok, counts, offsets, pool_src,
-                         slot_to_pool, pool_w, stream, true, pc,
-                         reinterpret_cast<const uint32_t*>(tok_s),
-                         sa_by_token ? static_cast<uint32_t*>(nullptr) : reinterpret_cast<uint32_t*>(pool_s));
     if (rc) return rc;
     if (o.debug_validate && (rc = check_routing_flag(ws, L, stream))) return rc;
+    // an upper bound on the tiles of the second table (the grid's extra
+    // workgroups find no tile and return)
+    const int64_t TKn = (int64_t)T * K;
+    const unsigned dec_grid_rows =
+        (unsigned)(plan.rm ? TKn / dec_rows(plan.rm) + (s->E < TKn ? s->E : TKn) + 1 : 0);
 
     GemmArgs g1;
     memset(&g1, 0, sizeof g1);
@@ -440,7 +492,7 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     g1.act_s = act_s;
     g1.I = I;
     g1.fast_math = o.fast_math ? 1 : 0;
-    if (decode) {
+    if (plan.l1) {
         if (sa_by_token) {
             g1.SA = tok_s;  // token-major words [T][H/128]
             g1.sa_step = 4;
@@ -448,8 +500,8 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
         }
         g1.mtiles = reinterpret_cast<const MTile*>(ws + L.mtiles64);
         g1.num_mtiles = reinterpret_cast<const int32_t*>(ws + L.num_mtiles64);
-        hipLaunchKernelGGL(k_gemm_l1_decode, dim3((unsigned)(L.max_mtiles64 * g1.ntiles)),
-                           dim3(kGemmThreads), 0, stream, g1);
+        hipLaunchKernelGGL(plan.rm == 1 ? k_gemm_l1_decode : k_gemm_l1_t128,
+                           dim3(dec_grid_rows * (unsigned)g1.ntiles), dim3(kGemmThreads), 0, stream, g1);
     } else {
         hipLaunchKernelGGL(k_gemm_l1, dim3(gemm_grid(L.max_mtiles * g1.ntiles)), dim3(kGemmThreads), 0,
                            stream, g1);
@@ -468,12 +520,17 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     g2.N = H;
     g2.ntiles = H / kBN;
     g2.out = l2_out;
-    if (decode)
-        hipLaunchKernelGGL(k_gemm_l2_decode, dim3((unsigned)(L.max_mtiles64 * g2.ntiles)),
-                           dim3(kGemmThreads), 0, stream, g2);
-    else
+    if (plan.l2) {
+        g2.mtiles = reinterpret_cast<const MTile*>(ws + L.mtiles64);
+        g2.num_mtiles = reinterpret_cast<const int32_t*>(ws + L.num_mtiles64);
+        hipLaunchKernelGGL(plan.rm == 1 ? k_gemm_l2_decode : k_gemm_l2_t128,
+                           dim3(dec_grid_rows * (unsigned)g2.ntiles), dim3(kGemmThreads), 0, stream, g2);
+    } else {
+        g2.mtiles = reinterpret_cast<const MTile*>(ws + L.mtiles);
+        g2.num_mtiles = reinterpret_cast<const int32_t*>(ws + L.num_mtiles);
         hipLaunchKernelGGL(k_gemm_l2, dim3(gemm_grid(L.max_mtiles * g2.ntiles)), dim3(kGemmThreads), 0,
                            stream, g2);
+    }
     prof_mark(pc, MOE_STAGE_GEMM_L2, stream);
 
     {

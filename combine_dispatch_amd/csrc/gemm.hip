@@ -1157,8 +1157,15 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
 // A-scale words from the token-major words by token (GemmArgs SA = those
 // words, sa_step = 4), so the call needs no pool copy of them; as those are
 // 64 scattered words, wave 0 alone fetches them into a copy all waves read.
-template <int MODE>
+template <int MODE, int RM>
 __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, float* s_w) {
+    constexpr int ROWS = dec_rows(RM);         // tile rows: 2 RM MFMA row tiles per wave
+    constexpr int STAGES = dec_stages(RM);
+    constexpr int SA_BYTES = dec_stage_a(RM);
+    constexpr int SB_OFF = SA_BYTES + kDecStageB;            // A-scale copies
+    constexpr int SBW_OFF = SB_OFF + dec_stage_sa(RM);       // B-scale words
+    constexpr int STAGE_BYTES = dec_stage_bytes(RM);
+    constexpr int LPS = 2 * RM + 4 + RM + 1;   // loads per wave and K step
     const int tid = threadIdx.x;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -1173,20 +1180,19 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
     const int Kdim = g.Kdim, nk = Kdim / kBK, b_ld = Kdim / 2;
 
     // per-lane load offsets
-    // A: chunk q = tid + 256 i (i = 0, 1) is LDS row q/8, physical chunk q%8
+    // A: chunk q = tid + 256 i (i < 2 RM) is LDS row q/8, physical chunk q%8
     // holding logical chunk (q%8) ^ ((row/2)%8); L1 rows come from the
     // token-major codes through pool_tok (indices clamped into the buffer).
-    uint32_t a_off0, a_off1;
+    uint32_t a_off[2 * RM];
     {
         const uint32_t tmax = (uint32_t)(g.T - 1);
-        auto aoff = [&](int i) {
+#pragma unroll
+        for (int i = 0; i < 2 * RM; ++i) {
             const int row = (tid >> 3) + 32 * i;
             const int lch = (tid & 7) ^ ((row >> 1) & 7);
             const uint32_t arow = MODE == kL1 ? min((uint32_t)g.pool_tok[row0 + row], tmax) : (uint32_t)row;
-            return arow * (uint32_t)Kdim + 16u * (uint32_t)lch;
-        };
-        a_off0 = aoff(0);
-        a_off1 = aoff(1);
+            a_off[i] = arow * (uint32_t)Kdim + 16u * (uint32_t)lch;
+        }
     }
     // B: chunk q = tid + 256 i (i = 0..3) is LDS row q/4 (weight row
     // b_row_narrow of it), physical chunk q%4 holding logical (q%4) ^ ((row/4)%4)
@@ -1197,11 +1203,11 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
         return (uint32_t)((b_row_narrow<MODE>(nt, row, g.I) - brow0) * b_ld + 16 * lch);
     };
     const uint32_t b_off0 = boff(0), b_off1 = boff(1), b_off2 = boff(2), b_off3 = boff(3);
-    // scale words: A row row0 + lane into the wave's copy -- L1 straight from
-    // the token-major words of its token (no pool copy of them), L2 from the
-    // packed k-major words of the pool rows; B: LDS word tid is the word of
-    // LDS B row tid
-    const bool sa_tok = MODE == kL1 && g.sa_by_token;
+    // scale words: A rows row0 + lane (+ 64) into the wave's copy -- L1 with
+    // sa_by_token straight from the token-major words of its token (no pool
+    // copy of them), else from the packed k-major words of the pool rows;
+    // B: LDS word tid is the word of LDS B row tid
+    const bool sa_tok = RM == 1 && MODE == kL1 && g.sa_by_token;
     uint32_t sa_off;
     if (sa_tok)
         sa_off = 4u * min((uint32_t)g.pool_tok[row0 + lane], (uint32_t)(g.T - 1)) * (uint32_t)nk;
@@ -1214,32 +1220,34 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
     const int64_t sb_step = (int64_t)g.N * 4;
     const uint8_t* sb_base = g.SB + (int64_t)e * nk * sb_step + (int64_t)brow0 * 4;
 
-    if (MODE == kL1 && tid < kDecRows) s_w[tid] = g.pool_w[row0 + tid];  // rows past the tile: unused
+    if (MODE == kL1 && tid < ROWS) s_w[tid] = g.pool_w[row0 + tid];  // rows past the tile: unused
 
-    auto stage = [&](int k) { return lds + (k % kDecStages) * kDecStageBytes; };
+    auto stage = [&](int k) { return lds + (k % STAGES) * STAGE_BYTES; };
     auto issue = [&](int k) __attribute__((always_inline)) {
         const uint32_t st = lds_addr(stage(k));
         const uint32_t wa = st + 1024u * wid;
-        dma_x4(wa, a_base + k * kBK, a_off0);
-        dma_x4(wa + 4096, a_base + k * kBK, a_off1);
-        const uint32_t wb = st + kDecStageA + 1024u * wid;
+#pragma unroll
+        for (int i = 0; i < 2 * RM; ++i) dma_x4(wa + 4096u * i, a_base + k * kBK, a_off[i]);
+        const uint32_t wb = st + SA_BYTES + 1024u * wid;
         dma_x4(wb, b_base + k * (kBK / 2), b_off0);
         dma_x4(wb + 4096, b_base + k * (kBK / 2), b_off1);
         dma_x4(wb + 8192, b_base + k * (kBK / 2), b_off2);
         dma_x4(wb + 12288, b_base + k * (kBK / 2), b_off3);
+        const uint32_t wsa = st + SB_OFF + 4u * ROWS * wid;
         if (sa_tok) {
             // the rows' words scattered by token: wave 0 fetches them into
             // the shared copy; the other waves keep the per-wave count of
             // loads with a contiguous stand-in (the B words again) into
             // their own unused slot
             if (wid == 0)
-                dma_x1(st + kDecStageA + kDecStageB, sa_base + k * g.sa_step, sa_off);
+                dma_x1(st + SB_OFF, sa_base + k * g.sa_step, sa_off);
             else
-                dma_x1(st + kDecStageA + kDecStageB + 256u * wid, sb_base + k * sb_step, sb_off);
+                dma_x1(wsa, sb_base + k * sb_step, sb_off);
         } else {
-            dma_x1(st + kDecStageA + kDecStageB + 256u * wid, sa_base + k * g.sa_step, sa_off);
+#pragma unroll
+            for (int i = 0; i < RM; ++i) dma_x1(wsa + 256u * i, sa_base + k * g.sa_step, sa_off + 256u * i);
         }
-        dma_x1(st + kDecStageA + kDecStageB + kDecStageSA + 256u * wid, sb_base + k * sb_step, sb_off);
+        dma_x1(st + SBW_OFF + 256u * wid, sb_base + k * sb_step, sb_off);
     };
 
     // this wave's column tiles (b_row_narrow): L1 gate and up of group wid,
@@ -1248,54 +1256,44 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
     const int jn1 = MODE == kL1 ? wid + 4 : 2 * wid + 1;
     const int a_sw = (l32 >> 1) & 7, b_sw = (l32 >> 2) & 3;
     const int hs = 16 * h;
-    v16f acc[2][2];
+    v16f acc[2 * RM][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2 * RM; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    constexpr int kAhead = kDecStages - 1;  // K steps whose loads are in flight
+    constexpr int kAhead = STAGES - 1;  // K steps whose loads are in flight
 #pragma unroll
     for (int k = 0; k < kAhead; ++k)
         if (k < nk) issue(k);
     for (int k = 0; k < nk; ++k) {
-        // step k's loads have landed (the later steps' may still fly: 8
+        // step k's loads have landed (the later steps' may still fly: LPS
         // loads per step and wave), and every wave is done reading step
         // k-1's stage, which step k + kAhead then refills
         const int later = min(kAhead - 1, nk - 1 - k);
-        if (later >= 3)
-            asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        else if (later == 2)
-            asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (later >= 2)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LPS) : "memory");
         else if (later == 1)
-            asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPS) : "memory");
         else
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (k + kAhead < nk) issue(k + kAhead);
         const uint8_t* sA = stage(k);
-        const uint8_t* sB = sA + kDecStageA;
-        const uint8_t* sSA = sB + kDecStageB + (sa_tok ? 0 : 256 * wid);  // by token: wave 0's copy
-        const uint8_t* sSB = sB + kDecStageB + kDecStageSA;
-        int wa0 = *reinterpret_cast<const int*>(sSA + 4 * l32);
-        int wa1 = *reinterpret_cast<const int*>(sSA + 4 * (32 + l32));
+        const uint8_t* sB = sA + SA_BYTES;
+        const uint8_t* sSA = sA + SB_OFF + (sa_tok ? 0 : 4 * ROWS * wid);  // by token: wave 0's copy
+        const uint8_t* sSB = sA + SBW_OFF;
+        int wa[2 * RM];
+#pragma unroll
+        for (int i = 0; i < 2 * RM; ++i)
+            wa[i] = (int)(*reinterpret_cast<const uint32_t*>(sSA + 4 * (32 * i + l32)) >> hs);
         int wb0 = *reinterpret_cast<const int*>(sSB + 4 * (32 * jn0 + l32));
         int wb1 = *reinterpret_cast<const int*>(sSB + 4 * (32 * jn1 + l32));
-        wa0 = (int)((uint32_t)wa0 >> hs);
-        wa1 = (int)((uint32_t)wa1 >> hs);
         wb0 = (int)((uint32_t)wb0 >> hs);
         wb1 = (int)((uint32_t)wb1 >> hs);
         auto sub = [&](auto sconst) __attribute__((always_inline)) {
             constexpr int S = decltype(sconst)::value;
-            v8i a[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const uint8_t* rowp = sA + (32 * i + l32) * kBK;
-                const uint4 v0 = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * S + h) ^ a_sw));
-                const uint4 v1 = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * S + 2 + h) ^ a_sw));
-                a[i] = v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-            }
             v8i b[2];
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
@@ -1304,11 +1302,16 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
                 b[jj] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2 * RM; ++i) {
+                const uint8_t* rowp = sA + (32 * i + l32) * kBK;
+                const uint4 v0 = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * S + h) ^ a_sw));
+                const uint4 v1 = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * S + 2 + h) ^ a_sw));
+                const v8i a = v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
                     acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        a[i], b[jj], acc[i][jj], 0, 4, S, i ? wa1 : wa0, S, jj ? wb1 : wb0);
+                        a, b[jj], acc[i][jj], 0, 4, S, wa[i], S, jj ? wb1 : wb0);
+            }
         };
         sub(std::integral_constant<int, 0>{});
         sub(std::integral_constant<int, 1>{});
@@ -1323,7 +1326,7 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
         const __amdgpu_buffer_rsrc_t out_rs = rows_rsrc(out_base, nrows * N * 2);
         const int col = 64 * wid + 2 * l32;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 2 * RM; ++i) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int lrow = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -1341,7 +1344,7 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
         const uint32_t bshift = 8u * (uint32_t)(l32 & 3);
         __syncthreads();  // s_w visible
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 2 * RM; ++i) {
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
                 const int lrow0 = 32 * i + 8 * rq + 4 * h;
@@ -1403,14 +1406,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_l2(GemmArgs args) {
 
 
 __global__ __launch_bounds__(kGemmThreads, kDecWorkgroupsPerCU) void k_gemm_l1_decode(GemmArgs args) {
-    __shared__ __attribute__((aligned(16))) uint8_t st[kDecStages * kDecStageBytes];
-    __shared__ float s_w[kDecRows];
-    gemm_decode<kL1>(args, st, s_w);
+    __shared__ __attribute__((aligned(16))) uint8_t st[dec_stages(1) * dec_stage_bytes(1)];
+    __shared__ float s_w[dec_rows(1)];
+    gemm_decode<kL1, 1>(args, st, s_w);
 }
 
 __global__ __launch_bounds__(kGemmThreads, kDecWorkgroupsPerCU) void k_gemm_l2_decode(GemmArgs args) {
-    __shared__ __attribute__((aligned(16))) uint8_t st[kDecStages * kDecStageBytes];
-    gemm_decode<kL2>(args, st, nullptr);
+    __shared__ __attribute__((aligned(16))) uint8_t st[dec_stages(1) * dec_stage_bytes(1)];
+    gemm_decode<kL2, 1>(args, st, nullptr);
+}
+
+__global__ __launch_bounds__(kGemmThreads, kDecWorkgroupsPerCU) void k_gemm_l1_t128(GemmArgs args) {
+    __shared__ __attribute__((aligned(16))) uint8_t st[dec_stages(2) * dec_stage_bytes(2)];
+    __shared__ float s_w[dec_rows(2)];
+    gemm_decode<kL1, 2>(args, st, s_w);
+}
+
+__global__ __launch_bounds__(kGemmThreads, kDecWorkgroupsPerCU) void k_gemm_l2_t128(GemmArgs args) {
+    __shared__ __attribute__((aligned(16))) uint8_t st[dec_stages(2) * dec_stage_bytes(2)];
+    gemm_decode<kL2, 2>(args, st, nullptr);
 }
 
 }  // namespace moe

@@ -30,17 +30,21 @@ struct MTile {
     int32_t expert, row0, nrows, pad;
 };
 
-// Decode-shaped GEMMs (batches whose experts hold few rows): tiles of at most
-// kDecRows rows, one workgroup per tile and n-tile, kDecStages LDS stages of
-// kDecStageBytes (two workgroups fit one CU).
+// Tile-per-workgroup GEMMs (batches whose experts hold few rows, and short
+// reductions): tiles of at most 64 * RM rows (RM = 1 or 2) x 256 columns, one
+// workgroup per tile and n-tile, dec_stages(RM) LDS stages of
+// dec_stage_bytes(RM) each, so that two workgroups fit one CU.
 constexpr int kDecRows = 64;
-constexpr int kDecStages = 3;
-constexpr int kDecWorkgroupsPerCU = 2;  // by LDS: kDecStages * kDecStageBytes each
-constexpr int kDecStageA = kDecRows * kBK;      // e4m3 rows
-constexpr int kDecStageB = kBN * kBK / 2;       // e2m1 rows
-constexpr int kDecStageSA = 4 * kDecRows * 4;   // each wave's copy of the 64 rows' scale words
+constexpr int kDecWorkgroupsPerCU = 2;
+constexpr int dec_rows(int rm) { return kDecRows * rm; }
+constexpr int dec_stage_a(int rm) { return dec_rows(rm) * kBK; }      // e4m3 rows
+constexpr int kDecStageB = kBN * kBK / 2;                             // e2m1 rows
+constexpr int dec_stage_sa(int rm) { return 4 * dec_rows(rm) * 4; }   // each wave's copy of the rows' scale words
 constexpr int kDecStageSB = kBN * 4;
-constexpr int kDecStageBytes = kDecStageA + kDecStageB + kDecStageSA + kDecStageSB;
+constexpr int dec_stage_bytes(int rm) { return dec_stage_a(rm) + kDecStageB + dec_stage_sa(rm) + kDecStageSB; }
+constexpr int dec_stages(int rm) { return rm == 1 ? 3 : 2; }
+static_assert(kDecWorkgroupsPerCU * dec_stages(1) * dec_stage_bytes(1) <= 160 * 1024, "LDS");
+static_assert(kDecWorkgroupsPerCU * dec_stages(2) * dec_stage_bytes(2) <= 160 * 1024, "LDS");
 
 // Tile records a persistent GEMM workgroup keeps in LDS: the launch must give
 // no workgroup more tiles than this (at most ceil(ceil(tiles / 8) / (grid / 8))).
@@ -93,7 +97,7 @@ __global__ void k_route(const int64_t* __restrict__ topk_idx, const float* __res
                         float* __restrict__ pool_w, int32_t* __restrict__ pool_tok,
                         const uint32_t* __restrict__ tok_s, int W, int64_t cap,
                         uint32_t* __restrict__ pool_s, MTile* __restrict__ mtiles64,
-                        int32_t* __restrict__ num_mtiles64);
+                        int32_t* __restrict__ num_mtiles64, int dec_rows);
 __global__ void k_route_scan(const int32_t* __restrict__ seg_hist,
                              const int32_t* __restrict__ seg_err, int nseg, int E,
                              int32_t* __restrict__ seg_base, int32_t* __restrict__ counts,
@@ -113,6 +117,19 @@ __global__ void k_quantise_count(const uint16_t* __restrict__ x, int64_t T, int 
                                  const int64_t* __restrict__ topk_idx, int64_t TK, int E, int ncount,
                                  int32_t* __restrict__ seg_hist, int32_t* __restrict__ seg_err,
                                  int32_t* __restrict__ blk_hist, int32_t* __restrict__ blk_err);
+// a1-a4 in one launch for batches of at most kRouteWaves * kSegSlots slots
+// (dynamic LDS: route_lds_bytes(E)); block 0 routes, the rest quantise.
+constexpr int64_t kRouteSingleMax = (int64_t)kRouteWaves * kSegSlots;
+__global__ void k_quantise_route(const uint16_t* __restrict__ x, int64_t T, int H, int tpb,
+                                 uint8_t* __restrict__ x_q, uint8_t* __restrict__ tok_s,
+                                 const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
+                                 int64_t TK, int E, int nbits, int K, int32_t* __restrict__ counts,
+                                 int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
+                                 int32_t* __restrict__ num_mtiles, int32_t* __restrict__ err_flag,
+                                 int32_t* __restrict__ pool_src, int32_t* __restrict__ slot_to_pool,
+                                 float* __restrict__ pool_w, int32_t* __restrict__ pool_tok,
+                                 MTile* __restrict__ mtiles64, int32_t* __restrict__ num_mtiles64,
+                                 int dec_rows);
 __global__ void k_pool_scales(const uint32_t* __restrict__ tok_s, int W,
                               const int32_t* __restrict__ pool_tok,
                               const int32_t* __restrict__ offsets, int E, int64_t cap,
@@ -136,5 +153,7 @@ __global__ void k_gemm_l1(GemmArgs args);
 __global__ void k_gemm_l2(GemmArgs args);
 __global__ void k_gemm_l1_decode(GemmArgs args);
 __global__ void k_gemm_l2_decode(GemmArgs args);
+__global__ void k_gemm_l1_t128(GemmArgs args);
+__global__ void k_gemm_l2_t128(GemmArgs args);
 
 }  // namespace moe

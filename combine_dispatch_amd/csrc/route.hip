@@ -267,16 +267,20 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int32_t* 
 // packed k-major layout (word (w, r) at w * cap + r), one thread per row in
 // the order of the rows.  Block 0 also writes counts, offsets, the GEMM's
 // expert-major m-tile table (and with mtiles64 set the same rows in tiles
-// of at most kDecRows rows) and the routing error flag.
-__global__ __launch_bounds__(kRouteThreads) void k_route(
-    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int64_t TK, int E,
+// of at most dec_rows rows) and the routing error flag.
+// SINGLE: the only block of a batch of at most kRouteWaves * kSegSlots slots,
+// which counts its own slots instead of reading blk_hist / blk_err (so it
+// needs no counting pass before it).
+template <bool SINGLE>
+__device__ __forceinline__ void route_block(
+    int b, const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int64_t TK, int E,
     int nbits, int K, const int32_t* __restrict__ blk_hist, const int32_t* __restrict__ blk_err,
     int nblk, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     MTile* __restrict__ mtiles, int32_t* __restrict__ num_mtiles, int32_t* __restrict__ err_flag,
     int32_t* __restrict__ pool_src, int32_t* __restrict__ slot_to_pool, float* __restrict__ pool_w,
     int32_t* __restrict__ pool_tok, const uint32_t* __restrict__ tok_s, int W, int64_t cap,
-    uint32_t* __restrict__ pool_s, MTile* __restrict__ mtiles64, int32_t* __restrict__ num_mtiles64) {
-    extern __shared__ int32_t lds[];
+    uint32_t* __restrict__ pool_s, MTile* __restrict__ mtiles64, int32_t* __restrict__ num_mtiles64,
+    int dec_rows, int32_t* lds /* route_lds_bytes(E) */) {
     int32_t* s_tot = lds;                     // [E] expert totals
     int32_t* s_pre = s_tot + E;               // [E] rows of the expert in blocks before this one
     int32_t* s_run = s_pre + E;               // [kRouteWaves][E] per-wave counts, then running bases
@@ -287,7 +291,6 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
     __shared__ int32_t s_w[kRouteWaves];
     __shared__ int32_t s_nrows;
     const int tid = threadIdx.x, wv = tid / kWave, lane = tid % kWave;
-    const int b = blockIdx.x;
     const int64_t nseg = (TK + kSegSlots - 1) / kSegSlots;
     const int64_t seg = (int64_t)b * kRouteWaves + wv;
     const int64_t f0 = seg * kSegSlots;
@@ -297,6 +300,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
     constexpr int kIt = kSegSlots / kWave;
     int sl_e[kIt];
     float sl_w[kIt];
+    int bad = 0;  // an index >= E (SINGLE: this block is the whole batch)
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
         const int64_t f = f0 + it * kWave + lane;
@@ -308,6 +312,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
                 sl_e[it] = (int)v;
                 sl_w[it] = topk_w[f];
             }
+            bad |= v >= E;
         }
     }
     int32_t* h = s_run + wv * E;
@@ -318,10 +323,20 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
         if (sl_e[it] >= 0) atomicAdd(&h[sl_e[it]], 1);
 
     // expert totals and rows in earlier blocks: P threads per expert, each
-    // summing a run of the blocks' histograms
+    // summing a run of the blocks' histograms (SINGLE: the block's own counts)
+    if (SINGLE) {
+        __syncthreads();  // the waves' counts complete
+        for (int e = tid; e < E; e += kRouteThreads) {
+            int tot = 0;
+#pragma unroll
+            for (int w = 0; w < kRouteWaves; ++w) tot += s_run[w * E + e];
+            s_tot[e] = tot;
+            s_pre[e] = 0;
+        }
+    }
     int P = 1;
     while (2 * P * E <= kRouteThreads) P *= 2;
-    for (int x = tid; x < P * E; x += kRouteThreads) {
+    for (int x = tid; x < (SINGLE ? 0 : P * E); x += kRouteThreads) {
         const int e = x % E, p = x / E;
         const int C = (nblk + P - 1) / P;
         const int b0 = min(nblk, p * C), b1 = min(nblk, b0 + C);
@@ -341,7 +356,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
         }
     }
     __syncthreads();
-    if (P > 1)
+    if (!SINGLE && P > 1)
         for (int e = tid; e < E; e += kRouteThreads) {
             int tot = 0, pre = 0;
             for (int p = 0; p < P; ++p) {
@@ -474,32 +489,33 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
             }
             toff += nt;
         }
-        // the same rows in 64-row tiles, for the decode-shaped GEMMs
+        // the same rows in tiles of dec_rows rows, for the tile-per-workgroup GEMMs
         int ntot64 = 0;
         if (mtiles64) {
             int my64 = 0;
             for (int j = 0; j < ept; ++j) {
                 const int e = ept * tid + j;
-                if (e < E) my64 += (s_tot[e] + kDecRows - 1) / kDecRows;
+                if (e < E) my64 += (s_tot[e] + dec_rows - 1) / dec_rows;
             }
             int t64 = block_exclusive_scan(my64, &ntot64, s_w);
             for (int j = 0; j < ept; ++j) {
                 const int e = ept * tid + j;
                 if (e >= E) continue;
-                const int cnt = s_tot[e], nt = (cnt + kDecRows - 1) / kDecRows;
+                const int cnt = s_tot[e], nt = (cnt + dec_rows - 1) / dec_rows;
                 for (int i = 0; i < nt; ++i) {
                     MTile m;
                     m.expert = e;
-                    m.row0 = s_off[e] + i * kDecRows;
-                    m.nrows = min(kDecRows, cnt - i * kDecRows);
+                    m.row0 = s_off[e] + i * dec_rows;
+                    m.nrows = min(dec_rows, cnt - i * dec_rows);
                     m.pad = 0;
                     mtiles64[t64 + i] = m;
                 }
                 t64 += nt;
             }
         }
-        int err = 0;
-        for (int bb = tid; bb < nblk; bb += kRouteThreads) err |= blk_err[bb];
+        int err = SINGLE ? bad : 0;
+        if (!SINGLE)
+            for (int bb = tid; bb < nblk; bb += kRouteThreads) err |= blk_err[bb];
         err = __syncthreads_or(err);
         if (tid == 0) {
             offsets[E] = R;
@@ -508,6 +524,21 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
             *err_flag = err ? 1 : 0;
         }
     }
+}
+
+__global__ __launch_bounds__(kRouteThreads) void k_route(
+    const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int64_t TK, int E,
+    int nbits, int K, const int32_t* __restrict__ blk_hist, const int32_t* __restrict__ blk_err,
+    int nblk, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    MTile* __restrict__ mtiles, int32_t* __restrict__ num_mtiles, int32_t* __restrict__ err_flag,
+    int32_t* __restrict__ pool_src, int32_t* __restrict__ slot_to_pool, float* __restrict__ pool_w,
+    int32_t* __restrict__ pool_tok, const uint32_t* __restrict__ tok_s, int W, int64_t cap,
+    uint32_t* __restrict__ pool_s, MTile* __restrict__ mtiles64, int32_t* __restrict__ num_mtiles64,
+    int dec_rows) {
+    extern __shared__ int32_t lds[];
+    route_block<false>(blockIdx.x, topk_idx, topk_w, TK, E, nbits, K, blk_hist, blk_err, nblk, counts,
+                       offsets, mtiles, num_mtiles, err_flag, pool_src, slot_to_pool, pool_w, pool_tok,
+                       tok_s, W, cap, pool_s, mtiles64, num_mtiles64, dec_rows, lds);
 }
 
 // a4: gather + quantise.  A block takes tpb consecutive token rows (as many
@@ -611,6 +642,29 @@ __global__ __launch_bounds__(256) void k_quantise_count(const uint16_t* __restri
         route_count_block(topk_idx, TK, E, seg_hist, seg_err, blockIdx.x, lds_hist, blk_hist, blk_err);
     else
         dispatch_fp8_block(x, T, H, 1, tpb, nullptr, x_q, nullptr, tok_s, blockIdx.x - ncount);
+}
+
+// The fused layer's first launch for batches of at most kRouteWaves *
+// kSegSlots slots: block 0 does all of a1-a3 (it is the only routing block,
+// so it counts its own slots and no block waits for another), the others
+// quantise the token rows token-major.  The pool rows' A-scale words need
+// every token's words, so they are not gathered here.
+__global__ __launch_bounds__(256) void k_quantise_route(
+    const uint16_t* __restrict__ x, int64_t T, int H, int tpb, uint8_t* __restrict__ x_q,
+    uint8_t* __restrict__ tok_s, const int64_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, int64_t TK, int E, int nbits, int K,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
+    int32_t* __restrict__ num_mtiles, int32_t* __restrict__ err_flag,
+    int32_t* __restrict__ pool_src, int32_t* __restrict__ slot_to_pool, float* __restrict__ pool_w,
+    int32_t* __restrict__ pool_tok, MTile* __restrict__ mtiles64, int32_t* __restrict__ num_mtiles64,
+    int dec_rows) {
+    extern __shared__ int32_t lds[];
+    if (blockIdx.x == 0)
+        route_block<true>(0, topk_idx, topk_w, TK, E, nbits, K, nullptr, nullptr, 1, counts, offsets,
+                          mtiles, num_mtiles, err_flag, pool_src, slot_to_pool, pool_w, pool_tok,
+                          nullptr, H / 128, 0, nullptr, mtiles64, num_mtiles64, dec_rows, lds);
+    else
+        dispatch_fp8_block(x, T, H, 1, tpb, nullptr, x_q, nullptr, tok_s, blockIdx.x - 1);
 }
 
 // A-scale words of the pool rows in packed k-major order (the layout the L1

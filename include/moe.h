@@ -60,7 +60,20 @@ typedef struct {
     float activation_clamp;   /* NaN (default) = none; any other value -> MOE_ERR_UNSUPPORTED */
     int32_t debug_validate;   /* 1: synchronise after routing and return
                                  MOE_ERR_BAD_ROUTING if an expert index was >= E */
+    int32_t gemm_tiles;       /* which grouped-GEMM kernels run (same results
+                                 up to the summation order inside each MFMA
+                                 block, which all of them share):
+                                 MOE_TILES_AUTO (default): chosen by shape;
+                                 MOE_TILES_PERSISTENT: 256-row tiles, one
+                                 workgroup per CU working through its tiles;
+                                 MOE_TILES_64 / MOE_TILES_128: 64- or 128-row
+                                 tiles, one workgroup each.  The last two need
+                                 the one-launch routing (ceil(T*K/1024) * E <=
+                                 65536), else MOE_ERR_UNSUPPORTED; any other
+                                 value -> MOE_ERR_INVALID_ARG */
 } moe_options_t;
+
+enum { MOE_TILES_AUTO = 0, MOE_TILES_PERSISTENT = 1, MOE_TILES_64 = 2, MOE_TILES_128 = 3 };
 
 enum {
     MOE_OK = 0,

@@ -22,9 +22,11 @@ extern "C" {
 enum {
     MOE_STAGE_WEIGHT_SCALES = 0, /* weight scales -> packed k-major words (canonical entry only) */
     MOE_STAGE_DISPATCH,        /* a4: e4m3 quantisation of the token rows; a1 per-segment
-                                  expert histogram in the same launch */
+                                  expert histogram in the same launch (with at most 1024
+                                  slots, T*K, all of a1-a3 in that launch) */
     MOE_STAGE_ROUTE_SCAN,      /* a2: offsets, segment bases, m-tile tables; in the one-launch
-                                  routing (k_route) also a3 */
+                                  routing (k_route) also a3; empty when the dispatch launch
+                                  routed */
     MOE_STAGE_ROUTE_SCATTER,   /* a3: stable rank -> pool_src, slot_to_pool, pool_w, pool_tok
                                   (an empty interval when a3 ran in the one launch above) */
     MOE_STAGE_POOL_SCALES,     /* a4: the pool rows' scale words gathered by token (empty when

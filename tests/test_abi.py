@@ -53,6 +53,7 @@ def test_status_strings(moe):
 def test_default_options(moe):
     o = moe.moe_default_options()
     assert o.fast_math == 1 and o.debug_validate == 0 and o.activation_clamp != o.activation_clamp
+    assert o.gemm_tiles == moe.MOE_TILES_AUTO
 
 
 def test_workspace_sizing(moe):
@@ -100,6 +101,19 @@ def test_host_side_errors_need_no_device(moe):
     o = moe.options(activation_clamp=3.0)
     assert L.moe_fused_forward(ctypes.byref(s), ctypes.byref(o), *[null] * 8, null, 0,
                                null) == moe.MOE_ERR_UNSUPPORTED
+    # unknown GEMM tiling
+    o = moe.options(gemm_tiles=7)
+    assert L.moe_fused_forward(ctypes.byref(s), ctypes.byref(o), *[null] * 8, null, 0,
+                               null) == moe.MOE_ERR_INVALID_ARG
+    # forced tile-per-workgroup GEMMs on a shape whose routing takes two
+    # launches (ceil(T*K / 1024) * E > 65536): refused before any launch or
+    # dereference (the pointers below are never touched)
+    big = moe.MoeShape(8192, 256, 128, 1024, 16)
+    fake = ctypes.c_void_p(1 << 20)
+    for tiles in (moe.MOE_TILES_64, moe.MOE_TILES_128):
+        o = moe.options(gemm_tiles=tiles)
+        assert L.moe_fused_forward(ctypes.byref(big), ctypes.byref(o), *[fake] * 8, fake, 1 << 40,
+                                   null) == moe.MOE_ERR_UNSUPPORTED
     # unknown payload
     assert L.moe_dispatch(ctypes.byref(s), null, null, null, 7, *[null] * 7, null, 0,
                           null) == moe.MOE_ERR_INVALID_ARG

@@ -154,6 +154,39 @@ def test_forward_is_deterministic():
     np.testing.assert_array_equal(view(ws1, inp, "x_q"), view(ws2, inp, "x_q"))
 
 
+# Every GEMM kernel family (gemm_tiles: persistent 256-row tiles, 64- and
+# 128-row tiles with one workgroup each) accumulates each output in the same
+# K order with the same MFMA blocks, so all give the same bits.  The cases:
+# several tiles per expert with ragged tails and masked slots, the narrow
+# tile edges (32/33/64/65/256/257 rows), the decode edges (1..128 rows, an
+# empty expert), many experts mostly empty, one token, the largest top-k.
+TILE_CASES = [SMALL[1], SMALL[10], SMALL[11], SMALL[3], SMALL[9], SMALL[8],
+              dict(T=1000, H=1024, I=512, E=5, K=2, routing="zipf", seed=52, mask_p=0.05)]
+TILE_IDS = ["ragged", "tile_edges", "decode_edges", "sparse", "t1", "k64", "multi"]
+
+
+@pytest.mark.parametrize("case", TILE_CASES, ids=TILE_IDS)
+def test_gemm_tile_kernels_agree(case):
+    import combine_dispatch_amd as moe
+    inp = small_inputs(case)
+    say("case", case)
+    dev = to_dev(inp)
+    outs = {}
+    for tiles in (moe.MOE_TILES_PERSISTENT, moe.MOE_TILES_64, moe.MOE_TILES_128, moe.MOE_TILES_AUTO):
+        say("gemm_tiles", tiles)
+        y, ws = run_forward(inp, dev, opts=moe.options(gemm_tiles=tiles))
+        R = int(view(ws, inp, "offsets")[-1])
+        outs[tiles] = (y, {n: view(ws, inp, n, R) for n in ("act_q", "act_s", "l2_out")})
+    y0, m0 = outs[moe.MOE_TILES_PERSISTENT]
+    for tiles, (y, m) in outs.items():
+        for n in m0:
+            np.testing.assert_array_equal(m[n], m0[n], err_msg=f"{n}, gemm_tiles {tiles}")
+        np.testing.assert_array_equal(y, y0, err_msg=f"y, gemm_tiles {tiles}")
+    # and the common result is the oracle's, to the layer's bars
+    y_ref = oracle.forward(inp)
+    check_y(y0, y_ref, inp["topk_idx"])
+
+
 # ----------------------------------------------------------------------------
 # dispatch and combine entry points on their own
 # ----------------------------------------------------------------------------
