@@ -1,16 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the fused MoE layer on one MI355X.
 
-One step = one moe_fused_forward_packed call over the whole batch of the
+One step = one moe_fused_forward_prepacked call over the whole batch of the
 workload: dispatch (routing histogram, prefix sum, stable rank, gather + e4m3
 quantisation) -> L1 grouped GEMM with the SwiGLU*w / e4m3 epilogue -> L2
 grouped GEMM -> combine.  Inputs are seeded synthetic tensors already resident
-in HBM when the timed region starts.  The weight scales are laid out once
-before timing (moe_pack_weight_scales: weights are constant across calls, and
-the pages' fused entry also takes pre-transformed weights); the same number of
-steps of moe_fused_forward, which re-lays them every call, is timed after the
-main region and reported as ms_per_step_canonical_scales.  --scales canonical
-times that path instead.
+in HBM when the timed region starts.  The weights are laid out once before
+timing (moe_pack_weights: FP4 codes tile-blocked, scales packed; weights are
+constant across calls, and the pages' fused entry also takes pre-transformed
+weights); the same number of steps of moe_fused_forward, which takes the
+weights as given and re-lays the scales every call, is timed after the main
+region and reported as ms_per_step_canonical.  --weights packed-scales times
+moe_fused_forward_packed (codes as given, scales packed once), --weights
+canonical times moe_fused_forward.
 
 Prints ONE JSON line (rank 0):
   value        whole-layer TFLOP/s = 6*R*H*I / step time (R = routed rows)
@@ -55,9 +57,10 @@ def parse():
                    help="tiny | small | prefill | skewed | many")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample (0 = skip)")
-    p.add_argument("--scales", choices=("packed", "canonical"), default="packed",
-                   help="packed: weight scales laid out once before timing (default); "
-                        "canonical: moe_fused_forward re-lays them every step")
+    p.add_argument("--weights", choices=("prepacked", "packed-scales", "canonical"), default="prepacked",
+                   help="prepacked: codes and scales laid out once before timing (moe_pack_weights, "
+                        "default); packed-scales: scales laid out once, codes as given; canonical: "
+                        "moe_fused_forward re-lays the scales every step")
     p.add_argument("--graph", action="store_true",
                    help="also capture one moe_fused_forward_packed step into a HIP graph and report the replayed step "
                         "time (ms_per_step_graph) beside the main number")
@@ -148,20 +151,26 @@ def main():
     stream = torch.cuda.current_stream()
     packed = torch.empty(moe.moe_packed_scales_bytes(H, I, E), dtype=torch.uint8, device=dev)
     moe.moe_pack_weight_scales(d["S1"], d["S2"], packed, E=E, H=H, I=I, stream=stream)
+    prepacked = torch.empty(moe.moe_packed_weights_bytes(H, I, E), dtype=torch.uint8, device=dev)
+    moe.moe_pack_weights(d["W1q"], d["S1"], d["W2q"], d["S2"], prepacked, E=E, H=H, I=I, stream=stream)
 
     opts = moe.options(gemm_tiles={"auto": moe.MOE_TILES_AUTO, "persistent": moe.MOE_TILES_PERSISTENT,
                                    "64": moe.MOE_TILES_64, "128": moe.MOE_TILES_128}[a.gemm_tiles])
 
-    def step_packed():
-        moe.moe_fused_forward_packed(d["x"], d["topk_idx"], d["topk_w"], d["W1q"], d["W2q"],
-                                     packed, y, ws, opts=opts, E=E, I=I, stream=stream)
+    def call(mode, st):
+        if mode == "prepacked":
+            moe.moe_fused_forward_prepacked(d["x"], d["topk_idx"], d["topk_w"], prepacked, y, ws, E=E, I=I,
+                                            opts=opts, stream=st)
+        elif mode == "packed-scales":
+            moe.moe_fused_forward_packed(d["x"], d["topk_idx"], d["topk_w"], d["W1q"], d["W2q"],
+                                         packed, y, ws, opts=opts, E=E, I=I, stream=st)
+        else:
+            moe.moe_fused_forward(d["x"], d["topk_idx"], d["topk_w"], d["W1q"], d["S1"], d["W2q"],
+                                  d["S2"], y, ws, opts=opts, E=E, I=I, stream=st)
 
-    def step_canonical():
-        moe.moe_fused_forward(d["x"], d["topk_idx"], d["topk_w"], d["W1q"], d["S1"], d["W2q"],
-                              d["S2"], y, ws, opts=opts, E=E, I=I, stream=stream)
-
-    step, other = ((step_packed, step_canonical) if a.scales == "packed"
-                   else (step_canonical, step_packed))
+    other_mode = "canonical" if a.weights != "canonical" else "prepacked"
+    step = lambda: call(a.weights, stream)
+    other = lambda: call(other_mode, stream)
 
     # warm-up: at least `warmup` steps and at least `warmup_ms` of GPU time
     # (the clocks take a few hundred milliseconds of load to settle)
@@ -234,15 +243,12 @@ def main():
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
         with torch.cuda.stream(cap):
-            moe.moe_fused_forward_packed(d["x"], d["topk_idx"], d["topk_w"], d["W1q"], d["W2q"],
-                                         packed, y, ws, opts=opts, E=E, I=I, stream=cap)
+            call(a.weights, cap)
         stream.wait_stream(cap)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            moe.moe_fused_forward_packed(d["x"], d["topk_idx"], d["topk_w"], d["W1q"], d["W2q"],
-                                         packed, y, ws, opts=opts, E=E, I=I,
-                                         stream=torch.cuda.current_stream())
+            call(a.weights, torch.cuda.current_stream())
         for _ in range(3):
             graph.replay()
         torch.cuda.synchronize()
@@ -322,8 +328,11 @@ def main():
         "data": "synthetic (seeded; see moe_inputs)",
         "config": {"workload": f"{a.workload}: T={T} H={H} I={I} E={E} K={K} routing={cfg['routing']}",
                    "T": T, "H": H, "I": I, "E": E, "K": K, "routed_rows": R,
-                   "weight_scales": ("packed once before timing (moe_pack_weight_scales)"
-                                     if a.scales == "packed" else "re-laid every step"),
+                   "weights": {"prepacked": "codes tile-blocked and scales packed once before timing "
+                                            "(moe_pack_weights)",
+                               "packed-scales": "codes as given, scales packed once before timing "
+                                                "(moe_pack_weight_scales)",
+                               "canonical": "as given, scales re-laid every step"}[a.weights],
                    "parallelism": "single GPU, all experts local", "gemm_tiles": a.gemm_tiles},
         "routed_rows_per_s": round(rows_s, 1),
         "frac_of_fp8_peak": round(tflops / PEAK_TFLOPS, 4),
@@ -337,8 +346,7 @@ def main():
             "combine_gbs": round(comb_bytes / (per_launch["combine"] * 1e-3) / 1e9, 1),
             "hbm_peak_gbs": PEAK_HBM_GBS,
         },
-        ("ms_per_step_canonical_scales" if a.scales == "packed"
-         else "ms_per_step_packed_scales"): round(other_ms, 4),
+        f"ms_per_step_{other_mode}": round(other_ms, 4),
         "cold_ms_per_step": round(cold_ms, 4),
         **({"ms_per_step_graph": round(graph_ms, 4)} if graph_ms is not None else {}),
         "wall_s_timed": round(wall, 4),

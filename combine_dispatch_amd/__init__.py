@@ -38,6 +38,7 @@ EXPORTED = ("moe_default_options", "moe_workspace_bytes", "moe_dispatch_workspac
             "moe_fused_forward", "moe_dispatch", "moe_combine", "moe_workspace_views",
             "moe_status_string", "moe_profile_start", "moe_profile_stop",
             "moe_profile_stage_name", "moe_packed_scales_bytes", "moe_pack_weight_scales",
+            "moe_packed_weights_bytes", "moe_pack_weights", "moe_fused_forward_prepacked",
             "moe_fused_forward_packed", "moe_fused_forward_packed_noalloc")
 PROFILE_STAGES = 8
 
@@ -91,6 +92,13 @@ def lib():
         L.moe_fused_forward_packed.argtypes = [shp, ctypes.POINTER(MoeOptions), vp, vp, vp, vp,
                                                vp, vp, vp, vp, sz, vp]
         L.moe_fused_forward_packed.restype = i32
+        L.moe_packed_weights_bytes.argtypes = [shp]
+        L.moe_packed_weights_bytes.restype = sz
+        L.moe_pack_weights.argtypes = [shp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_pack_weights.restype = i32
+        L.moe_fused_forward_prepacked.argtypes = [shp, ctypes.POINTER(MoeOptions), vp, vp, vp, vp, vp,
+                                                  vp, sz, vp]
+        L.moe_fused_forward_prepacked.restype = i32
         L.moe_fused_forward_packed_noalloc.argtypes = [shp, ctypes.POINTER(MoeOptions), vp, vp, vp,
                                                        vp, vp, vp, vp, vp]
         L.moe_fused_forward_packed_noalloc.restype = i32
@@ -203,6 +211,34 @@ def moe_fused_forward_packed(x, topk_idx, topk_w, W1q, W2q, packed, y, workspace
                                           _ptr(y), _ptr(workspace),
                                           workspace.numel() * workspace.element_size(),
                                           _stream(stream)), "moe_fused_forward_packed")
+
+
+def moe_packed_weights_bytes(H: int, I: int, E: int) -> int:
+    """Bytes of the buffer moe_pack_weights fills (0 on a bad shape)."""
+    return int(lib().moe_packed_weights_bytes(ctypes.byref(MoeShape(1, H, I, E, 1))))
+
+
+def moe_pack_weights(W1q, S1, W2q, S2, packed, E: int, H: int, I: int, stream=None) -> None:
+    """Lay every weight (FP4 codes tile-blocked, scales packed) out once for
+    moe_fused_forward_prepacked; ``packed`` is a uint8 device tensor of at
+    least moe_packed_weights_bytes(H, I, E) bytes."""
+    shape = MoeShape(1, H, I, E, 1)
+    _check(lib().moe_pack_weights(ctypes.byref(shape), _ptr(W1q), _ptr(S1), _ptr(W2q), _ptr(S2),
+                                  _ptr(packed), packed.numel() * packed.element_size(), _stream(stream)),
+           "moe_pack_weights")
+
+
+def moe_fused_forward_prepacked(x, topk_idx, topk_w, packed, y, workspace, E: int, I: int, opts=None,
+                                stream=None) -> None:
+    """moe_fused_forward with every weight read from the buffer moe_pack_weights filled."""
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    shape = MoeShape(T, H, I, E, K)
+    o = ctypes.byref(opts) if opts is not None else None
+    _check(lib().moe_fused_forward_prepacked(ctypes.byref(shape), o, _ptr(x), _ptr(topk_idx),
+                                             _ptr(topk_w), _ptr(packed), _ptr(y), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(),
+                                             _stream(stream)), "moe_fused_forward_prepacked")
 
 
 def moe_fused_forward_packed_noalloc(x, topk_idx, topk_w, W1q, W2q, packed, y, opts=None,

@@ -97,6 +97,14 @@ size_t packed_total_bytes(const moe_shape_t* s) {
     return align_up(packed_s1_bytes(s)) + (size_t)s->E * s->H * (s->I / 32);
 }
 
+// Tile-blocked weights (moe_pack_weights): W1's codes, W2's codes, then the
+// packed weight scales, each from a 256-byte boundary.
+size_t tiled_w1_bytes(const moe_shape_t* s) { return (size_t)s->E * 2 * s->I * (s->H / 2); }
+size_t tiled_w2_bytes(const moe_shape_t* s) { return (size_t)s->E * s->H * (s->I / 2); }
+size_t tiled_w2_offset(const moe_shape_t* s) { return align_up(tiled_w1_bytes(s)); }
+size_t tiled_scales_offset(const moe_shape_t* s) { return tiled_w2_offset(s) + align_up(tiled_w2_bytes(s)); }
+size_t tiled_total_bytes(const moe_shape_t* s) { return tiled_scales_offset(s) + packed_total_bytes(s); }
+
 // Weight scales (ue8m0 [E][N][Kdim/32], rows of Kdim/128 words) -> the packed
 // k-major words the GEMMs load per K step, for both layers.
 void launch_pack_scales(const moe_shape_t* s, const uint8_t* S1, const uint8_t* S2, uint8_t* s1t,
@@ -369,7 +377,8 @@ namespace {
 int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
                   const int64_t* topk_idx, const float* topk_w, const uint8_t* W1q,
                   const uint8_t* S1, const uint8_t* W2q, const uint8_t* S2, const uint8_t* packed,
-                  void* y, void* workspace, size_t workspace_bytes, moe_stream_t stream_) {
+                  void* y, void* workspace, size_t workspace_bytes, moe_stream_t stream_,
+                  bool b_tiled = false) {
     if (!shape_basic_ok(s)) return MOE_ERR_INVALID_ARG;
     const moe_options_t o = opt ? *opt : moe_default_options();
     if (!isnan(o.activation_clamp)) return MOE_ERR_UNSUPPORTED;
@@ -477,6 +486,7 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     g1.A = x_q;
     g1.SA = pool_s;
     g1.B = W1q;
+    g1.b_tiled = b_tiled ? 1 : 0;
     g1.SB = s1t;
     g1.sa_step = 4 * L.cap;
     g1.act_s_step = 4 * L.cap;
@@ -584,6 +594,47 @@ int moe_fused_forward_packed(const moe_shape_t* s, const moe_options_t* opt, con
     return fused_forward(s, opt, x, topk_idx, topk_w, W1q, nullptr, W2q, nullptr,
                          static_cast<const uint8_t*>(packed_scales), y, workspace,
                          workspace_bytes, stream);
+}
+
+size_t moe_packed_weights_bytes(const moe_shape_t* s) {
+    if (!shape_basic_ok(s) || s->H % kBN || s->I % 128) return 0;
+    return tiled_total_bytes(s);
+}
+
+int moe_pack_weights(const moe_shape_t* s, const uint8_t* W1q, const uint8_t* S1, const uint8_t* W2q,
+                     const uint8_t* S2, void* packed, size_t packed_bytes, moe_stream_t stream_) {
+    if (!shape_basic_ok(s)) return MOE_ERR_INVALID_ARG;
+    if (s->H % kBN || s->I % 128) return MOE_ERR_UNSUPPORTED;
+    if (!W1q || !W2q || !S1 || !S2 || !packed) return MOE_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(W1q) | reinterpret_cast<uintptr_t>(W2q)) % 16 ||
+        (reinterpret_cast<uintptr_t>(S1) | reinterpret_cast<uintptr_t>(S2)) % 4 ||
+        reinterpret_cast<uintptr_t>(packed) % kAlign)
+        return MOE_ERR_INVALID_ARG;
+    if (packed_bytes < tiled_total_bytes(s)) return MOE_ERR_WORKSPACE;
+    if (!device_ok()) return MOE_ERR_DEVICE;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    uint8_t* p = static_cast<uint8_t*>(packed);
+    const int H = s->H, I = s->I, E = s->E;
+    const int64_t c1 = (int64_t)tiled_w1_bytes(s) / 16, c2 = (int64_t)tiled_w2_bytes(s) / 16;
+    hipLaunchKernelGGL(k_pack_weights_tiled, dim3((unsigned)((c1 + 255) / 256)), dim3(256), 0, stream, W1q, p,
+                       E, 2 * I, H, I, 1);
+    hipLaunchKernelGGL(k_pack_weights_tiled, dim3((unsigned)((c2 + 255) / 256)), dim3(256), 0, stream, W2q,
+                       p + tiled_w2_offset(s), E, H, I, I, 0);
+    uint8_t* sc = p + tiled_scales_offset(s);
+    launch_pack_scales(s, S1, S2, sc, sc + align_up(packed_s1_bytes(s)), stream);
+    return launch_status();
+}
+
+int moe_fused_forward_prepacked(const moe_shape_t* s, const moe_options_t* opt, const void* x,
+                                const int64_t* topk_idx, const float* topk_w, const void* packed_weights,
+                                void* y, void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+    if (!packed_weights) return MOE_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(packed_weights) % kAlign) return MOE_ERR_INVALID_ARG;
+    if (!shape_basic_ok(s)) return MOE_ERR_INVALID_ARG;
+    const uint8_t* p = static_cast<const uint8_t*>(packed_weights);
+    const bool sized = s->H % kBN == 0 && s->I % 128 == 0;  // else refused below, before any use
+    return fused_forward(s, opt, x, topk_idx, topk_w, p, nullptr, sized ? p + tiled_w2_offset(s) : p, nullptr,
+                         sized ? p + tiled_scales_offset(s) : p, y, workspace, workspace_bytes, stream, true);
 }
 
 int moe_fused_forward_packed_noalloc(const moe_shape_t* s, const moe_options_t* opt,

@@ -271,11 +271,17 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     // physical chunk q%4, logical chunk (q%4) ^ ((row/4)%4).
     const int b_chunk = (tid & 3) ^ ((tid >> 4) & 3);
     const int b_ld = Kdim / 2;
+    // the B codes' row stride, bytes per K step and the I of the row order
+    // (tile-blocked: rows of a block 64 bytes apart, blocks of a tile
+    // consecutive, L1's up rows right after its 128 gate rows)
+    const int b_rs = g.b_tiled ? kBK / 2 : b_ld;
+    const int64_t b_ks = g.b_tiled ? (int64_t)kBTileBytes : kBK / 2;
+    const int bI = g.b_tiled ? 128 : g.I;
     // Load q (0..3) covers LDS B rows 64q + tid/4; with the column order of
     // b_row its expert rows differ from those of load 0 by a wave-uniform
     // number of rows, which goes into the scalar base.
     // (row offsets relative to the tile's first B row do not depend on the tile)
-    const uint32_t b_off = (uint32_t)((b_row<MODE>(0, (tid >> 2), g.I) - b_row<MODE>(0, 0, g.I)) * b_ld + 16 * b_chunk);
+    const uint32_t b_off = (uint32_t)((b_row<MODE>(0, (tid >> 2), bI) - b_row<MODE>(0, 0, bI)) * b_rs + 16 * b_chunk);
     // per-load lane offsets (in vector registers: the scalar registers hold
     // one base per operand, advanced by K each step)
     // (L1 gathers its A rows from token rows: there the offsets change per
@@ -284,9 +290,9 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
 #pragma unroll
     for (int p = 0; p < 8; ++p) lo.set_a(p, a_off + 32 * p * Kdim);
     const uint32_t b_off0 = b_off,
-                   b_off1 = b_off + (b_row<MODE>(0, 64, g.I) - b_row<MODE>(0, 0, g.I)) * b_ld,
-                   b_off2 = b_off + (b_row<MODE>(0, 128, g.I) - b_row<MODE>(0, 0, g.I)) * b_ld,
-                   b_off3 = b_off + (b_row<MODE>(0, 192, g.I) - b_row<MODE>(0, 0, g.I)) * b_ld;
+                   b_off1 = b_off + (b_row<MODE>(0, 64, bI) - b_row<MODE>(0, 0, bI)) * b_rs,
+                   b_off2 = b_off + (b_row<MODE>(0, 128, bI) - b_row<MODE>(0, 0, bI)) * b_rs,
+                   b_off3 = b_off + (b_row<MODE>(0, 192, bI) - b_row<MODE>(0, 0, bI)) * b_rs;
     // scales: packed k-major words, one 4-byte word (4 k-blocks) per row per
     // step, the words of a step contiguous over rows.  LDS word p of the A
     // scales is row tile p%2 of wave p/64, lane row (p%64)/2, so a lane's two
@@ -299,11 +305,11 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     const int64_t sb_step = (int64_t)g.N * 4;
     const uint32_t sb_off = (uint32_t)((b_row<MODE>(0, 32 * (tid & 7) + (tid >> 3), g.I) - b_row<MODE>(0, 0, g.I)) * 4);
     // the same lane offsets for the column order of narrow tiles
-    const uint32_t nb_off = (uint32_t)((b_row_narrow<MODE>(0, (tid >> 2), g.I) - b_row_narrow<MODE>(0, 0, g.I)) * b_ld + 16 * b_chunk);
+    const uint32_t nb_off = (uint32_t)((b_row_narrow<MODE>(0, (tid >> 2), bI) - b_row_narrow<MODE>(0, 0, bI)) * b_rs + 16 * b_chunk);
     const uint32_t nb_off0 = nb_off,
-                   nb_off1 = nb_off + (b_row_narrow<MODE>(0, 64, g.I) - b_row_narrow<MODE>(0, 0, g.I)) * b_ld,
-                   nb_off2 = nb_off + (b_row_narrow<MODE>(0, 128, g.I) - b_row_narrow<MODE>(0, 0, g.I)) * b_ld,
-                   nb_off3 = nb_off + (b_row_narrow<MODE>(0, 192, g.I) - b_row_narrow<MODE>(0, 0, g.I)) * b_ld;
+                   nb_off1 = nb_off + (b_row_narrow<MODE>(0, 64, bI) - b_row_narrow<MODE>(0, 0, bI)) * b_rs,
+                   nb_off2 = nb_off + (b_row_narrow<MODE>(0, 128, bI) - b_row_narrow<MODE>(0, 0, bI)) * b_rs,
+                   nb_off3 = nb_off + (b_row_narrow<MODE>(0, 192, bI) - b_row_narrow<MODE>(0, 0, bI)) * b_rs;
     const uint32_t nsb_off = (uint32_t)((b_row_narrow<MODE>(0, 32 * (tid & 7) + (tid >> 3), g.I) - b_row_narrow<MODE>(0, 0, g.I)) * 4);
     // column order of the tile whose loads go out when NAR below is 2: 1 for
     // a narrow tile (wave-uniform)
@@ -313,7 +319,8 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
     auto set_bases = [&]() __attribute__((always_inline)) {
         const int b_r0 = b_row<MODE>(nt, 0, g.I);
         a_base = MODE == kL1 ? g.A : g.A + (int64_t)row0 * Kdim;
-        b_base = g.B + ((int64_t)e * g.N + b_r0) * b_ld;
+        b_base = g.b_tiled ? g.B + ((int64_t)e * g.ntiles + nt) * (int64_t)nk * kBTileBytes
+                           : g.B + ((int64_t)e * g.N + b_r0) * b_ld;
         sa_base = g.SA + (int64_t)row0 * 4;
         sb_base = g.SB + (int64_t)e * (Kdim / 128) * sb_step + (int64_t)b_r0 * 4;
     };
@@ -368,7 +375,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs& g, uint8_t* st0,
             const uint32_t fo = p == 8 ? b_off0 : p == 9 ? b_off1 : p == 10 ? b_off2 : b_off3;
             const uint32_t no = p == 8 ? nb_off0 : p == 9 ? nb_off1 : p == 10 ? nb_off2 : nb_off3;
             const uint32_t off = NAR == 0 ? fo : NAR == 1 ? no : (lnar ? no : fo);
-            dma_x4(st + kStageA + w_dst16 + 4096 * (p - 8), b_base + k0 / 2, off);
+            dma_x4(st + kStageA + w_dst16 + 4096 * (p - 8), b_base + kk * b_ks, off);
         } else if (p == 12) {
             dma_x1(st + kStageA + kStageB + w_dst4, sa_base + kk * sa_step, lo.sa);
         } else if (p == 13) {
@@ -1197,10 +1204,14 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
     // B: chunk q = tid + 256 i (i = 0..3) is LDS row q/4 (weight row
     // b_row_narrow of it), physical chunk q%4 holding logical (q%4) ^ ((row/4)%4)
     const int brow0 = b_row_narrow<MODE>(nt, 0, g.I);
+    // tile-blocked codes: rows 64 bytes apart, L1's up rows right after its
+    // 128 gate rows, 16 KiB per K step
+    const int b_rs = g.b_tiled ? kBK / 2 : b_ld, bI = g.b_tiled ? 128 : g.I;
+    const int64_t b_ks = g.b_tiled ? (int64_t)kBTileBytes : kBK / 2;
     auto boff = [&](int i) {
         const int row = (tid >> 2) + 64 * i;
         const int lch = (tid & 3) ^ ((row >> 2) & 3);
-        return (uint32_t)((b_row_narrow<MODE>(nt, row, g.I) - brow0) * b_ld + 16 * lch);
+        return (uint32_t)((b_row_narrow<MODE>(0, row, bI) - b_row_narrow<MODE>(0, 0, bI)) * b_rs + 16 * lch);
     };
     const uint32_t b_off0 = boff(0), b_off1 = boff(1), b_off2 = boff(2), b_off3 = boff(3);
     // scale words: A rows row0 + lane (+ 64) into the wave's copy -- L1 with
@@ -1215,7 +1226,8 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
         sa_off = 4u * (uint32_t)lane;
     const uint32_t sb_off = (uint32_t)(4 * (b_row_narrow<MODE>(nt, tid, g.I) - brow0));
     const uint8_t* a_base = MODE == kL1 ? g.A : g.A + (int64_t)row0 * Kdim;
-    const uint8_t* b_base = g.B + ((int64_t)e * g.N + brow0) * b_ld;
+    const uint8_t* b_base = g.b_tiled ? g.B + ((int64_t)e * g.ntiles + nt) * (int64_t)nk * kBTileBytes
+                                      : g.B + ((int64_t)e * g.N + brow0) * b_ld;
     const uint8_t* sa_base = sa_tok ? g.SA : g.SA + (int64_t)row0 * 4;  // by token: token-major words
     const int64_t sb_step = (int64_t)g.N * 4;
     const uint8_t* sb_base = g.SB + (int64_t)e * nk * sb_step + (int64_t)brow0 * 4;
@@ -1229,10 +1241,10 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
 #pragma unroll
         for (int i = 0; i < 2 * RM; ++i) dma_x4(wa + 4096u * i, a_base + k * kBK, a_off[i]);
         const uint32_t wb = st + SA_BYTES + 1024u * wid;
-        dma_x4(wb, b_base + k * (kBK / 2), b_off0);
-        dma_x4(wb + 4096, b_base + k * (kBK / 2), b_off1);
-        dma_x4(wb + 8192, b_base + k * (kBK / 2), b_off2);
-        dma_x4(wb + 12288, b_base + k * (kBK / 2), b_off3);
+        dma_x4(wb, b_base + k * b_ks, b_off0);
+        dma_x4(wb + 4096, b_base + k * b_ks, b_off1);
+        dma_x4(wb + 8192, b_base + k * b_ks, b_off2);
+        dma_x4(wb + 12288, b_base + k * b_ks, b_off3);
         const uint32_t wsa = st + SB_OFF + 4u * ROWS * wid;
         if (sa_tok) {
             // the rows' words scattered by token: wave 0 fetches them into
@@ -1425,6 +1437,27 @@ __global__ __launch_bounds__(kGemmThreads, kDecWorkgroupsPerCU) void k_gemm_l1_t
 __global__ __launch_bounds__(kGemmThreads, kDecWorkgroupsPerCU) void k_gemm_l2_t128(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) uint8_t st[dec_stages(2) * dec_stage_bytes(2)];
     gemm_decode<kL2, 2>(args, st, nullptr);
+}
+
+// One 16-byte chunk per thread, in the order of the tile-blocked layout
+// (consecutive threads write consecutive chunks): block (e, nt, k) holds
+// rows r = 0..255 of 64 bytes, row r being weight row 256 nt + r (L2) or
+// gate row 128 nt + r / up row I + 128 nt + r - 128 (L1).
+__global__ __launch_bounds__(256) void k_pack_weights_tiled(const uint8_t* __restrict__ W,
+                                                           uint8_t* __restrict__ Wp, int E, int N,
+                                                           int Kdim, int I, int l1) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int nk = Kdim / kBK, ntiles = N / kBN;
+    const int64_t total = (int64_t)E * N * (Kdim / 2) / 16;
+    if (q >= total) return;
+    const int64_t blk = q >> 10;  // 1024 chunks per block
+    const int rem = (int)(q & 1023), r = rem >> 2, ch = rem & 3;
+    const int k = (int)(blk % nk);
+    const int64_t t = blk / nk;
+    const int nt = (int)(t % ntiles), e = (int)(t / ntiles);
+    const int w = l1 ? (r < 128 ? 0 : I) + 128 * nt + (r & 127) : kBN * nt + r;
+    const uint4 v = *reinterpret_cast<const uint4*>(W + ((int64_t)e * N + w) * (Kdim / 2) + k * (kBK / 2) + 16 * ch);
+    *reinterpret_cast<uint4*>(Wp + q * 16) = v;
 }
 
 }  // namespace moe

@@ -57,7 +57,7 @@ constexpr int kTileCache = 256;
 struct GemmArgs {
     const uint8_t* A;    // e4m3 [rows][Kdim]; L1: token rows [T][Kdim] (see pool_tok)
     const uint8_t* SA;   // packed k-major words [Kdim/128][cap rows]
-    const uint8_t* B;    // e2m1x2 [E][N][Kdim/2]
+    const uint8_t* B;    // e2m1x2 [E][N][Kdim/2], or with b_tiled the tile-blocked layout below
     const uint8_t* SB;   // packed k-major words per expert [E][Kdim/128][N]
     int64_t sa_step;     // bytes between K steps of SA (4 * cap)
     // L1: pool row r takes A row pool_tok[r] (entries past the routed rows may
@@ -77,6 +77,12 @@ struct GemmArgs {
     int32_t I;
     int32_t fast_math;
     int32_t sa_by_token;  // decode L1: SA = token-major words [T][Kdim/128], read by pool_tok
+    // B codes tile-blocked (moe_pack_weights): for expert e, n-tile nt and K
+    // step k one contiguous block of 256 rows x 64 bytes at
+    // ((e * ntiles + nt) * (Kdim/128) + k) * 16384, row r of the block being
+    // weight row 256 nt + r (L2) or, for L1, gate row 128 nt + r (r < 128)
+    // and up row I + 128 nt + r - 128 (r >= 128)
+    int32_t b_tiled;
     // L2 epilogue
     uint16_t* out;       // bf16 [rows][N]
 };
@@ -149,6 +155,11 @@ inline int tokens_per_block(int H) {
 __global__ void k_combine(const uint16_t* __restrict__ o, const int32_t* __restrict__ slot_to_pool,
                           const float* __restrict__ topk_w, int64_t T, int H, int K, int tpb,
                           uint16_t* __restrict__ y);
+// Weight codes [E][N][Kdim/2] -> the tile-blocked layout of GemmArgs.b_tiled
+// (l1: the L1 weights' gate/up n-tiles, I the intermediate size; else L2).
+constexpr int kBTileBytes = kBN * kBK / 2;
+__global__ void k_pack_weights_tiled(const uint8_t* __restrict__ W, uint8_t* __restrict__ Wp, int E,
+                                     int N, int Kdim, int I, int l1);
 __global__ void k_gemm_l1(GemmArgs args);
 __global__ void k_gemm_l2(GemmArgs args);
 __global__ void k_gemm_l1_decode(GemmArgs args);

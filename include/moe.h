@@ -163,6 +163,38 @@ int moe_fused_forward_packed(const moe_shape_t* s, const moe_options_t* opt /* N
                              moe_stream_t stream);
 
 /*
+ * Weights laid out once in the GEMMs' own layout, codes as well as scales
+ * (the pages' fused entry takes both transformed: [P1] "tests/test_mega_moe.py"
+ * snippet).  The FP4 codes are re-blocked so that what one GEMM K step of one
+ * 256-row n-tile reads is one contiguous 16 KiB block: for expert e, n-tile
+ * nt (L1: I/128 of them, each the 128 gate rows 128 nt.. and the 128 up rows
+ * I + 128 nt..; L2: H/256, rows 256 nt..) and K step k (128 wide), block
+ * ((e * ntiles + nt) * (K/128) + k) holds the tile's 256 rows in that order,
+ * 64 bytes (128 codes) each.  A K step then reads one stretch of memory
+ * instead of 256 rows a row-length apart.  Layout of the buffer: W1's blocks,
+ * W2's blocks from the next 256-byte boundary, then from the next the packed
+ * weight scales of moe_pack_weight_scales.
+ *
+ * moe_packed_weights_bytes: bytes of that buffer (host only; 0 on a bad or
+ * unsupported shape) -- the size of the weights plus that of the packed scales.
+ * moe_pack_weights: fills `packed` (device, 256-byte aligned, owned by the
+ * caller) from W1q, W2q (16-byte aligned) and S1, S2 (4-byte aligned), as
+ * given to moe_fused_forward.  Asynchronous on `stream`.  Errors as
+ * moe_pack_weight_scales.
+ * moe_fused_forward_prepacked: moe_fused_forward with every weight read from
+ * that buffer (filled for the same shape); the result is bit-identical to
+ * moe_fused_forward and moe_fused_forward_packed.  The buffer must stay
+ * unchanged while calls that read it are in flight.
+ */
+size_t moe_packed_weights_bytes(const moe_shape_t* s);
+int moe_pack_weights(const moe_shape_t* s, const uint8_t* W1q, const uint8_t* S1, const uint8_t* W2q,
+                     const uint8_t* S2, void* packed, size_t packed_bytes, moe_stream_t stream);
+int moe_fused_forward_prepacked(const moe_shape_t* s, const moe_options_t* opt /* NULL = defaults */,
+                                const void* x, const int64_t* topk_idx, const float* topk_w,
+                                const void* packed_weights, void* y, void* workspace,
+                                size_t workspace_bytes, moe_stream_t stream);
+
+/*
  * moe_fused_forward_packed without a workspace argument, for callers that
  * cannot allocate device memory around the call: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.  The

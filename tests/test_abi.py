@@ -123,6 +123,32 @@ def test_host_side_errors_need_no_device(moe):
     assert L.moe_combine(ctypes.byref(s), null, null, null, null, null) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_prepacked_weight_entry_points_host_side(moe):
+    L = moe.lib()
+    null = ctypes.c_void_p(0)
+    H, I, E = 7168, 2048, 32
+    w1, w2 = E * 2 * I * (H // 2), E * H * (I // 2)
+    up = lambda n: (n + 255) // 256 * 256
+    assert moe.moe_packed_weights_bytes(H, I, E) == up(w1) + up(w2) + moe.moe_packed_scales_bytes(H, I, E)
+    assert moe.moe_packed_weights_bytes(200, I, E) == 0
+    s = moe.MoeShape(16, 256, 128, 4, 2)
+    fake = ctypes.c_void_p(1 << 20)
+    # null or misaligned pointers, a short buffer: found before any device call
+    assert L.moe_pack_weights(ctypes.byref(s), null, fake, fake, fake, fake, 1 << 30, null) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(ctypes.byref(s), ctypes.c_void_p((1 << 20) + 8), fake, fake, fake, fake, 1 << 30,
+                              null) == moe.MOE_ERR_INVALID_ARG
+    need = moe.moe_packed_weights_bytes(256, 128, 4)
+    assert L.moe_pack_weights(ctypes.byref(s), fake, fake, fake, fake, fake, need - 1, null) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_pack_weights(ctypes.byref(moe.MoeShape(16, 200, 128, 4, 2)), fake, fake, fake, fake, fake,
+                              1 << 30, null) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_fused_forward_prepacked(ctypes.byref(s), None, fake, fake, fake, null, fake, fake, 1 << 30,
+                                         null) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_fused_forward_prepacked(ctypes.byref(s), None, fake, fake, fake, ctypes.c_void_p((1 << 20) + 16),
+                                         fake, fake, 1 << 30, null) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_fused_forward_prepacked(ctypes.byref(moe.MoeShape(16, 200, 128, 4, 2)), None, fake, fake, fake,
+                                         fake, fake, fake, 1 << 30, null) == moe.MOE_ERR_UNSUPPORTED
+
+
 def test_packed_scale_entry_points_host_side(moe):
     L = moe.lib()
     null = ctypes.c_void_p(0)

@@ -390,6 +390,65 @@ def test_packed_weight_scales(case):
     assert ei.value.status == moe.MOE_ERR_WORKSPACE
 
 
+def tile_blocked(W, l1: bool, I: int) -> np.ndarray:
+    """The documented tile-blocked layout of weight codes W [E][N][K/2]: per
+    expert, 256-row n-tile (L1: 128 gate rows then the 128 matching up rows)
+    and 128-wide K step, one block of 256 rows x 64 bytes."""
+    E, N, kb = W.shape
+    nk, nt = kb // 64, N // 256
+    if l1:
+        rows = np.concatenate([np.concatenate([np.arange(128 * t, 128 * t + 128),
+                                               I + np.arange(128 * t, 128 * t + 128)]) for t in range(nt)])
+    else:
+        rows = np.arange(N)
+    Wr = W[:, rows, :].reshape(E, nt, 256, nk, 64)
+    return np.ascontiguousarray(Wr.transpose(0, 1, 3, 2, 4)).reshape(-1)
+
+
+PREPACK_CASES = [SMALL[1], SMALL[10], SMALL[11], SMALL[6], TILE_CASES[6]]
+
+
+@pytest.mark.parametrize("case", PREPACK_CASES, ids=["ragged", "tile_edges", "decode_edges", "e257", "multi"])
+def test_prepacked_weights(case):
+    """moe_pack_weights writes the documented layout (W1's blocks, W2's from
+    the next 256-byte boundary, then the packed scales), and the prepacked
+    forward equals the canonical one bit for bit with every GEMM kernel."""
+    import combine_dispatch_amd as moe
+    inp = small_inputs(case)
+    say("case", case)
+    T, H, I, E, K = (inp[k] for k in ("T", "H", "I", "E", "K"))
+    dev = to_dev(inp)
+    nbytes = moe.moe_packed_weights_bytes(H, I, E)
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    moe.moe_pack_weights(dev["W1q"], dev["S1"], dev["W2q"], dev["S2"], packed, E=E, H=H, I=I)
+    raw = packed.cpu().numpy()
+    w1 = E * 2 * I * (H // 2)
+    off2 = (w1 + 255) // 256 * 256
+    w2 = E * H * (I // 2)
+    offs = off2 + (w2 + 255) // 256 * 256
+    np.testing.assert_array_equal(raw[:w1], tile_blocked(inp["W1q"], True, I))
+    np.testing.assert_array_equal(raw[off2:off2 + w2], tile_blocked(inp["W2q"], False, I))
+    sc = torch.empty(moe.moe_packed_scales_bytes(H, I, E), dtype=torch.uint8, device=DEV)
+    moe.moe_pack_weight_scales(dev["S1"], dev["S2"], sc, E=E, H=H, I=I)
+    np.testing.assert_array_equal(raw[offs:offs + sc.numel()], sc.cpu().numpy())
+    y_ref, ws_ref = run_forward(inp, dev)
+    R = int(view(ws_ref, inp, "offsets")[-1])
+    for tiles in (moe.MOE_TILES_AUTO, moe.MOE_TILES_PERSISTENT, moe.MOE_TILES_64):
+        say("gemm_tiles", tiles)
+        ws = torch.empty(moe.moe_workspace_bytes(T, H, I, E, K), dtype=torch.uint8, device=DEV)
+        y = torch.empty((T, H), dtype=torch.int16, device=DEV)
+        moe.moe_fused_forward_prepacked(dev["x"], dev["topk_idx"], dev["topk_w"], packed, y, ws, E=E, I=I,
+                                        opts=moe.options(gemm_tiles=tiles))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bf16_bits(y), y_ref)
+        for name in ("act_q", "act_s", "l2_out"):
+            np.testing.assert_array_equal(view(ws, inp, name, R), view(ws_ref, inp, name, R))
+    short = torch.empty(nbytes - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_pack_weights(dev["W1q"], dev["S1"], dev["W2q"], dev["S2"], short, E=E, H=H, I=I)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE
+
+
 def test_exact_math_option_also_within_tolerance():
     import combine_dispatch_amd as moe
     inp = small_inputs(SMALL[1])
