@@ -544,10 +544,10 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     prof_mark(pc, MOE_STAGE_GEMM_L2, stream);
 
     {
-        const int tpb = tokens_per_block(H);
-        hipLaunchKernelGGL(k_combine, dim3((unsigned)(((int64_t)T + tpb - 1) / tpb)), dim3(256), 0, stream,
-                           l2_out, slot_to_pool, static_cast<const float*>(nullptr), (int64_t)T, H,
-                           K, tpb, static_cast<uint16_t*>(y));
+        const int tpb = tokens_per_block(H), parts = combine_parts(T, H, tpb);
+        hipLaunchKernelGGL(k_combine, dim3((unsigned)(((int64_t)T + tpb - 1) / tpb * parts)), dim3(256), 0,
+                           stream, l2_out, slot_to_pool, static_cast<const float*>(nullptr), (int64_t)T, H,
+                           K, tpb, parts, static_cast<uint16_t*>(y));
     }
     prof_mark(pc, MOE_STAGE_COMBINE, stream);
     return launch_status();
@@ -716,10 +716,10 @@ int moe_combine(const moe_shape_t* s, const void* pool_out, const int32_t* slot_
     if (!pool_out || !slot_to_pool || !y) return MOE_ERR_INVALID_ARG;
     if (!device_ok()) return MOE_ERR_DEVICE;
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-    const int tpb = tokens_per_block(s->H);
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)(((int64_t)s->T + tpb - 1) / tpb)), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(pool_out), slot_to_pool, topk_w,
-                       (int64_t)s->T, s->H, s->K, tpb, static_cast<uint16_t*>(y));
+    const int tpb = tokens_per_block(s->H), parts = combine_parts(s->T, s->H, tpb);
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)(((int64_t)s->T + tpb - 1) / tpb * parts)), dim3(256), 0,
+                       stream, static_cast<const uint16_t*>(pool_out), slot_to_pool, topk_w,
+                       (int64_t)s->T, s->H, s->K, tpb, parts, static_cast<uint16_t*>(y));
     return launch_status();
 }
 

@@ -152,8 +152,16 @@ inline int tokens_per_block(int H) {
     const int t = 8192 / H;
     return t < 1 ? 1 : (t > kMaxBlockTokens ? kMaxBlockTokens : t);
 }
+// Blocks per group of tpb tokens: small batches split a block's columns
+// into up to four pieces so that the grid covers the GPU.
+inline int combine_parts(int64_t T, int H, int tpb) {
+    const int64_t blocks = (T + tpb - 1) / tpb;
+    if (blocks >= 1024) return 1;
+    const int64_t by_cols = ((int64_t)tpb * H + 2047) / 2048;  // at least 2048 columns a piece
+    return (int)(by_cols < 4 ? (by_cols < 1 ? 1 : by_cols) : 4);
+}
 __global__ void k_combine(const uint16_t* __restrict__ o, const int32_t* __restrict__ slot_to_pool,
-                          const float* __restrict__ topk_w, int64_t T, int H, int K, int tpb,
+                          const float* __restrict__ topk_w, int64_t T, int H, int K, int tpb, int nparts,
                           uint16_t* __restrict__ y);
 // Weight codes [E][N][Kdim/2] -> the tile-blocked layout of GemmArgs.b_tiled
 // (l1: the L1 weights' gate/up n-tiles, I the intermediate size; else L2).

@@ -755,9 +755,11 @@ __global__ __launch_bounds__(256) void k_dispatch_bf16(const uint16_t* __restric
     }
 }
 
-// a9: combine.  A block takes tpb consecutive tokens (tpb * H <= 8192 when
-// tpb > 1, so that small rows still fill the block); each lane owns 8
-// columns of up to four 2048-column chunks of the block's flat [tpb][H] span.
+// a9: combine.  A group of tpb consecutive tokens (tpb * H <= 8192 when
+// tpb > 1, so that small rows still fill a block) goes to nparts blocks, each
+// taking one piece of the group's flat [tpb][H] columns (nparts > 1 only for
+// small batches, whose groups alone would not cover the GPU); each lane owns
+// 8 columns of up to four 2048-column chunks of its block's piece.
 // The K pool rows behind every chunk are loaded first (4K independent loads
 // in flight per lane, the rate of a plain HBM read stream), then summed in
 // ascending k in fp32 starting from +0, then rounded to bf16.  Multiplies and
@@ -766,11 +768,12 @@ __global__ __launch_bounds__(256) void k_dispatch_bf16(const uint16_t* __restric
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
                                                 const int32_t* __restrict__ slot_to_pool,
                                                 const float* __restrict__ topk_w, int64_t T,
-                                                int H, int K, int tpb,
+                                                int H, int K, int tpb, int nparts,
                                                 uint16_t* __restrict__ y) {
     __shared__ int32_t rows[kMaxBlockTokens * 64];
     __shared__ float wts[kMaxBlockTokens * 64];
-    const int64_t t0 = (int64_t)blockIdx.x * tpb;
+    const int part = (int)(blockIdx.x % (unsigned)nparts);
+    const int64_t t0 = (int64_t)(blockIdx.x / (unsigned)nparts) * tpb;
     for (int i = threadIdx.x; i < tpb * K; i += 256) {
         const int64_t t = t0 + i / K;
         const bool in = t < T;
@@ -779,13 +782,17 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
     }
     __syncthreads();
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const int span = tpb * H;  // flat columns of the block's tokens
-    for (int c00 = threadIdx.x * 8; c00 < span; c00 += 4 * 256 * 8) {
+    // the block's share of the flat columns of its tokens: part `part` of
+    // nparts pieces of whole 8-column runs
+    const int span = tpb * H;
+    const int piece = ((span + nparts - 1) / nparts + 7) & ~7;
+    const int lo = part * piece, hi = min(span, lo + piece);
+    for (int c00 = lo + threadIdx.x * 8; c00 < hi; c00 += 4 * 256 * 8) {
         int tok[4], col[4];
 #pragma unroll
         for (int hh = 0; hh < 4; ++hh) {
             const int p = c00 + hh * 256 * 8;
-            const int j = p < span ? p / H : -1;  // H % 8 == 0: a lane's 8 columns share a token
+            const int j = p < hi ? p / H : -1;  // H % 8 == 0: a lane's 8 columns share a token
             tok[hh] = j;
             col[hh] = j >= 0 ? p - j * H : 0;
         }
