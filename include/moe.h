@@ -273,8 +273,9 @@ typedef struct {
     int64_t pool_tok;         /* int32 [cap]: token of pool row r (first R entries) */
     int64_t x_q, x_s;         /* e4m3 [T][H], words [T][H/128] */
     int64_t pool_s;           /* x_s words of the pool rows, packed k-major [H/128][cap];
-                                 not written when T*K <= 256 and T*K <= 64*E: such a call's
-                                 decode-shaped L1 GEMM reads x_s by token */
+                                 not written when the call runs the 64-row-tile GEMMs (by
+                                 default when T*K <= 64*E) with T*K <= 1024: their L1
+                                 GEMM then reads x_s by token */
     int64_t act_q, act_s;     /* e4m3 [cap][I], packed k-major words [I/128][cap] */
     int64_t l2_out;           /* bf16 [cap][H] */
     int64_t capacity_rows;    /* cap = T*K + tile padding */

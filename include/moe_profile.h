@@ -30,8 +30,8 @@ enum {
     MOE_STAGE_ROUTE_SCATTER,   /* a3: stable rank -> pool_src, slot_to_pool, pool_w, pool_tok
                                   (an empty interval when a3 ran in the one launch above) */
     MOE_STAGE_POOL_SCALES,     /* a4: the pool rows' scale words gathered by token (empty when
-                                  the L1 GEMM reads them by token: at most 256 routed slots
-                                  and at most 64 per expert on average) */
+                                  the L1 GEMM reads them by token: the 64-row-tile GEMMs
+                                  with at most 1024 routed slots) */
     MOE_STAGE_GEMM_L1,         /* a5-a7: L1 GEMM (gathers the token rows), SwiGLU*w, e4m3 requant */
     MOE_STAGE_GEMM_L2,         /* a8: L2 GEMM, bf16 rows */
     MOE_STAGE_COMBINE,         /* a9: top-k fp32 reduction to bf16 */

@@ -74,6 +74,6 @@ def view(workspace: torch.Tensor, inp: dict, name: str, rows: int | None = None)
 def uses_decode_path(inp: dict) -> bool:
     """Whether the fused layer leaves the workspace's pool_s unwritten: its
     decode-shaped GEMMs (at most 64 routed rows per expert on average) read
-    the A-scale words by token when there are at most 256 routed rows."""
+    the A-scale words by token when there are at most 1024 routed slots."""
     TK = inp["T"] * inp["K"]
-    return TK <= 64 * inp["E"] and TK <= 256
+    return TK <= 64 * inp["E"] and TK <= 1024
