@@ -1185,6 +1185,10 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
     const int row0 = __builtin_amdgcn_readfirstlane(rec.row0);
     const int nrows = __builtin_amdgcn_readfirstlane(rec.nrows);
     const int Kdim = g.Kdim, nk = Kdim / kBK, b_ld = Kdim / 2;
+    // 32-row MFMA row tiles that hold rows of this tile (wave-uniform): the
+    // others skip their MFMAs and epilogue.  (Their A rows are still loaded:
+    // a 4-byte stand-in load instead made the T = 128 L1 3 % slower.)
+    const int nrt = (nrows + 31) >> 5;
 
     // per-lane load offsets
     // A: chunk q = tid + 256 i (i < 2 RM) is LDS row q/8, physical chunk q%8
@@ -1239,7 +1243,9 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
         const uint32_t st = lds_addr(stage(k));
         const uint32_t wa = st + 1024u * wid;
 #pragma unroll
-        for (int i = 0; i < 2 * RM; ++i) dma_x4(wa + 4096u * i, a_base + k * kBK, a_off[i]);
+        for (int i = 0; i < 2 * RM; ++i) {
+            dma_x4(wa + 4096u * i, a_base + k * kBK, a_off[i]);
+        }
         const uint32_t wb = st + SA_BYTES + 1024u * wid;
         dma_x4(wb, b_base + k * b_ks, b_off0);
         dma_x4(wb + 4096, b_base + k * b_ks, b_off1);
@@ -1315,6 +1321,7 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
             }
 #pragma unroll
             for (int i = 0; i < 2 * RM; ++i) {
+                if (i >= nrt) continue;  // no rows
                 const uint8_t* rowp = sA + (32 * i + l32) * kBK;
                 const uint4 v0 = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * S + h) ^ a_sw));
                 const uint4 v1 = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * S + 2 + h) ^ a_sw));
@@ -1339,6 +1346,7 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
         const int col = 64 * wid + 2 * l32;
 #pragma unroll
         for (int i = 0; i < 2 * RM; ++i) {
+            if (i >= nrt) continue;  // no rows
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int lrow = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -1357,6 +1365,7 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
         __syncthreads();  // s_w visible
 #pragma unroll
         for (int i = 0; i < 2 * RM; ++i) {
+            if (i >= nrt) continue;  // no rows
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
                 const int lrow0 = 32 * i + 8 * rq + 4 * h;

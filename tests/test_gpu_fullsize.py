@@ -200,7 +200,18 @@ def test_full_compare(name):
     # the five workloads' y bar applies to the small-batch workload and to the
     # production widths; the mid case (I = 384) is held to it beyond its
     # activation differences
-    fullsize_check(inp, full=True, strict_y=name != "mid")
+    y, ws = fullsize_check(inp, full=True, strict_y=name != "mid")
+    # the prepacked-weight entry gives the same bits
+    import combine_dispatch_amd as moe
+    T, H, I, E = inp["T"], inp["H"], inp["I"], inp["E"]
+    dev = to_dev(inp)
+    pw = torch.empty(moe.moe_packed_weights_bytes(H, I, E), dtype=torch.uint8, device=DEV)
+    moe.moe_pack_weights(dev["W1q"], dev["S1"], dev["W2q"], dev["S2"], pw, E=E, H=H, I=I)
+    yp = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    moe.moe_fused_forward_prepacked(dev["x"], dev["topk_idx"], dev["topk_w"], pw, yp, ws, E=E, I=I)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_bits(yp), y)
+    say(name, "prepacked-weight entry bit-identical")
 
 
 @pytest.mark.parametrize("name", ["prefill", "skewed", "many"])
@@ -220,3 +231,11 @@ def test_workload_tile_edges(name):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bf16_bits(yp), y)
     say(name, "packed-scale entry bit-identical")
+    # and the prepacked-weight entry the benchmark times (tile-blocked codes)
+    del packed
+    pw = torch.empty(moe.moe_packed_weights_bytes(H, I, E), dtype=torch.uint8, device=DEV)
+    moe.moe_pack_weights(dev["W1q"], dev["S1"], dev["W2q"], dev["S2"], pw, E=E, H=H, I=I)
+    moe.moe_fused_forward_prepacked(dev["x"], dev["topk_idx"], dev["topk_w"], pw, yp, ws, E=E, I=I)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_bits(yp), y)
+    say(name, "prepacked-weight entry bit-identical")
