@@ -436,11 +436,14 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     const int64_t nq = ((int64_t)T + tpb - 1) / tpb;
     int rc = MOE_OK;
     if ((int64_t)T * K <= kRouteSingleMax) {
-        // one launch for a1-a4: block 0 routes the whole batch while the
-        // others quantise the token rows
-        hipLaunchKernelGGL(k_quantise_route, dim3((unsigned)(1 + nq)), dim3(256), route_lds_bytes(s->E),
+        // one launch for a1-a4: the first blocks route the batch (256 slots
+        // each, every one counting all slots itself) while the others
+        // quantise the token rows
+        const int64_t TKn = (int64_t)T * K;
+        const int nroute = (int)((TKn + kRouteThreads - 1) / kRouteThreads);
+        hipLaunchKernelGGL(k_quantise_route, dim3((unsigned)(nroute + nq)), dim3(256), route_lds_bytes(s->E),
                            stream, static_cast<const uint16_t*>(x), (int64_t)T, H, tpb, x_q, tok_s,
-                           topk_idx, topk_w, (int64_t)T * K, s->E, bits_for(s->E), K, counts, offsets,
+                           topk_idx, topk_w, TKn, s->E, bits_for(s->E), K, nroute, counts, offsets,
                            reinterpret_cast<MTile*>(ws + L.mtiles),
                            reinterpret_cast<int32_t*>(ws + L.num_mtiles),
                            reinterpret_cast<int32_t*>(ws + L.err_flag), pool_src, slot_to_pool, pool_w,

@@ -124,12 +124,13 @@ __global__ void k_quantise_count(const uint16_t* __restrict__ x, int64_t T, int 
                                  int32_t* __restrict__ seg_hist, int32_t* __restrict__ seg_err,
                                  int32_t* __restrict__ blk_hist, int32_t* __restrict__ blk_err);
 // a1-a4 in one launch for batches of at most kRouteWaves * kSegSlots slots
-// (dynamic LDS: route_lds_bytes(E)); block 0 routes, the rest quantise.
+// (dynamic LDS: route_lds_bytes(E)): blocks [0, nroute = ceil(T*K / 256))
+// route, the rest quantise.
 constexpr int64_t kRouteSingleMax = (int64_t)kRouteWaves * kSegSlots;
 __global__ void k_quantise_route(const uint16_t* __restrict__ x, int64_t T, int H, int tpb,
                                  uint8_t* __restrict__ x_q, uint8_t* __restrict__ tok_s,
                                  const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
-                                 int64_t TK, int E, int nbits, int K, int32_t* __restrict__ counts,
+                                 int64_t TK, int E, int nbits, int K, int nroute, int32_t* __restrict__ counts,
                                  int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
                                  int32_t* __restrict__ num_mtiles, int32_t* __restrict__ err_flag,
                                  int32_t* __restrict__ pool_src, int32_t* __restrict__ slot_to_pool,

@@ -253,6 +253,74 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int32_t* 
     return base + inc - v;
 }
 
+// The routing's outputs besides the per-slot ones, written by one block from
+// the expert totals s_tot and offsets s_off in its LDS (R rows in all, err
+// set if an expert index was >= E): counts, offsets[E+1], the expert-major
+// m-tile table (tiles of kBM rows) and, with mtiles64 set, the same rows in
+// tiles of dec_rows rows, and the error flag.  Thread tid owns experts
+// [ept tid, ept tid + ept); s_w: kRouteWaves words of scan scratch.
+__device__ __forceinline__ void route_write_tables(int E, int R, int err, const int32_t* s_tot,
+                                                   const int32_t* s_off, int32_t* s_w,
+                                                   int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                   MTile* __restrict__ mtiles, int32_t* __restrict__ num_mtiles,
+                                                   int32_t* __restrict__ err_flag, MTile* __restrict__ mtiles64,
+                                                   int32_t* __restrict__ num_mtiles64, int dec_rows) {
+    const int tid = threadIdx.x;
+    const int ept = (E + kRouteThreads - 1) / kRouteThreads;
+    int my_nt = 0;
+    for (int j = 0; j < ept; ++j) {
+        const int e = ept * tid + j;
+        if (e < E) my_nt += (s_tot[e] + kBM - 1) / kBM;
+    }
+    int ntot = 0;
+    int toff = block_exclusive_scan(my_nt, &ntot, s_w);
+    for (int j = 0; j < ept; ++j) {
+        const int e = ept * tid + j;
+        if (e >= E) continue;
+        const int cnt = s_tot[e], nt = (cnt + kBM - 1) / kBM;
+        counts[e] = cnt;
+        offsets[e] = s_off[e];
+        for (int i = 0; i < nt; ++i) {
+            MTile m;
+            m.expert = e;
+            m.row0 = s_off[e] + i * kBM;
+            m.nrows = min(kBM, cnt - i * kBM);
+            m.pad = 0;
+            mtiles[toff + i] = m;
+        }
+        toff += nt;
+    }
+    int ntot64 = 0;
+    if (mtiles64) {
+        int my64 = 0;
+        for (int j = 0; j < ept; ++j) {
+            const int e = ept * tid + j;
+            if (e < E) my64 += (s_tot[e] + dec_rows - 1) / dec_rows;
+        }
+        int t64 = block_exclusive_scan(my64, &ntot64, s_w);
+        for (int j = 0; j < ept; ++j) {
+            const int e = ept * tid + j;
+            if (e >= E) continue;
+            const int cnt = s_tot[e], nt = (cnt + dec_rows - 1) / dec_rows;
+            for (int i = 0; i < nt; ++i) {
+                MTile m;
+                m.expert = e;
+                m.row0 = s_off[e] + i * dec_rows;
+                m.nrows = min(dec_rows, cnt - i * dec_rows);
+                m.pad = 0;
+                mtiles64[t64 + i] = m;
+            }
+            t64 += nt;
+        }
+    }
+    if (tid == 0) {
+        offsets[E] = R;
+        *num_mtiles = ntot;
+        if (num_mtiles64) *num_mtiles64 = ntot64;
+        *err_flag = err ? 1 : 0;
+    }
+}
+
 // a2 + a3 + the pool rows' scale words, in one launch.  Block b takes the
 // kRouteWaves segments the counting pass's block b counted (wave w: segment
 // kRouteWaves*b + w) and works out for itself what a scan over that pass's
@@ -268,10 +336,6 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int32_t* 
 // the order of the rows.  Block 0 also writes counts, offsets, the GEMM's
 // expert-major m-tile table (and with mtiles64 set the same rows in tiles
 // of at most dec_rows rows) and the routing error flag.
-// SINGLE: the only block of a batch of at most kRouteWaves * kSegSlots slots,
-// which counts its own slots instead of reading blk_hist / blk_err (so it
-// needs no counting pass before it).
-template <bool SINGLE>
 __device__ __forceinline__ void route_block(
     int b, const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int64_t TK, int E,
     int nbits, int K, const int32_t* __restrict__ blk_hist, const int32_t* __restrict__ blk_err,
@@ -300,7 +364,6 @@ __device__ __forceinline__ void route_block(
     constexpr int kIt = kSegSlots / kWave;
     int sl_e[kIt];
     float sl_w[kIt];
-    int bad = 0;  // an index >= E (SINGLE: this block is the whole batch)
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
         const int64_t f = f0 + it * kWave + lane;
@@ -312,7 +375,6 @@ __device__ __forceinline__ void route_block(
                 sl_e[it] = (int)v;
                 sl_w[it] = topk_w[f];
             }
-            bad |= v >= E;
         }
     }
     int32_t* h = s_run + wv * E;
@@ -323,20 +385,10 @@ __device__ __forceinline__ void route_block(
         if (sl_e[it] >= 0) atomicAdd(&h[sl_e[it]], 1);
 
     // expert totals and rows in earlier blocks: P threads per expert, each
-    // summing a run of the blocks' histograms (SINGLE: the block's own counts)
-    if (SINGLE) {
-        __syncthreads();  // the waves' counts complete
-        for (int e = tid; e < E; e += kRouteThreads) {
-            int tot = 0;
-#pragma unroll
-            for (int w = 0; w < kRouteWaves; ++w) tot += s_run[w * E + e];
-            s_tot[e] = tot;
-            s_pre[e] = 0;
-        }
-    }
+    // summing a run of the blocks' histograms
     int P = 1;
     while (2 * P * E <= kRouteThreads) P *= 2;
-    for (int x = tid; x < (SINGLE ? 0 : P * E); x += kRouteThreads) {
+    for (int x = tid; x < P * E; x += kRouteThreads) {
         const int e = x % E, p = x / E;
         const int C = (nblk + P - 1) / P;
         const int b0 = min(nblk, p * C), b1 = min(nblk, b0 + C);
@@ -356,7 +408,7 @@ __device__ __forceinline__ void route_block(
         }
     }
     __syncthreads();
-    if (!SINGLE && P > 1)
+    if (P > 1)
         for (int e = tid; e < E; e += kRouteThreads) {
             int tot = 0, pre = 0;
             for (int p = 0; p < P; ++p) {
@@ -465,64 +517,11 @@ __device__ __forceinline__ void route_block(
     }
 
     if (b == 0) {
-        // counts, offsets, the expert-major m-tile table, the error flag
-        int my_nt = 0;
-        for (int j = 0; j < ept; ++j) {
-            const int e = ept * tid + j;
-            if (e < E) my_nt += (s_tot[e] + kBM - 1) / kBM;
-        }
-        int ntot = 0;
-        int toff = block_exclusive_scan(my_nt, &ntot, s_w);
-        for (int j = 0; j < ept; ++j) {
-            const int e = ept * tid + j;
-            if (e >= E) continue;
-            const int cnt = s_tot[e], nt = (cnt + kBM - 1) / kBM;
-            counts[e] = cnt;
-            offsets[e] = s_off[e];
-            for (int i = 0; i < nt; ++i) {
-                MTile m;
-                m.expert = e;
-                m.row0 = s_off[e] + i * kBM;
-                m.nrows = min(kBM, cnt - i * kBM);
-                m.pad = 0;
-                mtiles[toff + i] = m;
-            }
-            toff += nt;
-        }
-        // the same rows in tiles of dec_rows rows, for the tile-per-workgroup GEMMs
-        int ntot64 = 0;
-        if (mtiles64) {
-            int my64 = 0;
-            for (int j = 0; j < ept; ++j) {
-                const int e = ept * tid + j;
-                if (e < E) my64 += (s_tot[e] + dec_rows - 1) / dec_rows;
-            }
-            int t64 = block_exclusive_scan(my64, &ntot64, s_w);
-            for (int j = 0; j < ept; ++j) {
-                const int e = ept * tid + j;
-                if (e >= E) continue;
-                const int cnt = s_tot[e], nt = (cnt + dec_rows - 1) / dec_rows;
-                for (int i = 0; i < nt; ++i) {
-                    MTile m;
-                    m.expert = e;
-                    m.row0 = s_off[e] + i * dec_rows;
-                    m.nrows = min(dec_rows, cnt - i * dec_rows);
-                    m.pad = 0;
-                    mtiles64[t64 + i] = m;
-                }
-                t64 += nt;
-            }
-        }
-        int err = SINGLE ? bad : 0;
-        if (!SINGLE)
-            for (int bb = tid; bb < nblk; bb += kRouteThreads) err |= blk_err[bb];
+        int err = 0;
+        for (int bb = tid; bb < nblk; bb += kRouteThreads) err |= blk_err[bb];
         err = __syncthreads_or(err);
-        if (tid == 0) {
-            offsets[E] = R;
-            *num_mtiles = ntot;
-            if (num_mtiles64) *num_mtiles64 = ntot64;
-            *err_flag = err ? 1 : 0;
-        }
+        route_write_tables(E, R, err, s_tot, s_off, s_w, counts, offsets, mtiles, num_mtiles, err_flag,
+                           mtiles64, num_mtiles64, dec_rows);
     }
 }
 
@@ -536,7 +535,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(
     uint32_t* __restrict__ pool_s, MTile* __restrict__ mtiles64, int32_t* __restrict__ num_mtiles64,
     int dec_rows) {
     extern __shared__ int32_t lds[];
-    route_block<false>(blockIdx.x, topk_idx, topk_w, TK, E, nbits, K, blk_hist, blk_err, nblk, counts,
+    route_block(blockIdx.x, topk_idx, topk_w, TK, E, nbits, K, blk_hist, blk_err, nblk, counts,
                        offsets, mtiles, num_mtiles, err_flag, pool_src, slot_to_pool, pool_w, pool_tok,
                        tok_s, W, cap, pool_s, mtiles64, num_mtiles64, dec_rows, lds);
 }
@@ -644,27 +643,124 @@ __global__ __launch_bounds__(256) void k_quantise_count(const uint16_t* __restri
         dispatch_fp8_block(x, T, H, 1, tpb, nullptr, x_q, nullptr, tok_s, blockIdx.x - ncount);
 }
 
+// a1-a3 for a batch of at most kRouteWaves * kSegSlots slots, over nb =
+// ceil(T*K / 256) blocks of which no block waits for another: block b ranks
+// slots [256 b, 256 b + 256) (wave w: 64 of them) and counts every slot of
+// the batch itself (at most 1024 indices) for the expert totals, hence the
+// offsets, and the expert's rows before its range.  Block 0 also writes the
+// tables.  LDS: 7 E counters and kRouteWaves + 1 words.
+__device__ __forceinline__ void route_small_block(
+    int b, const int64_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int64_t TK, int E,
+    int nbits, int K, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    MTile* __restrict__ mtiles, int32_t* __restrict__ num_mtiles, int32_t* __restrict__ err_flag,
+    int32_t* __restrict__ pool_src, int32_t* __restrict__ slot_to_pool, float* __restrict__ pool_w,
+    int32_t* __restrict__ pool_tok, MTile* __restrict__ mtiles64, int32_t* __restrict__ num_mtiles64,
+    int dec_rows, int32_t* lds) {
+    int32_t* s_tot = lds;                      // [E] expert totals
+    int32_t* s_pre = s_tot + E;                // [E] the expert's slots before this block's range
+    int32_t* s_run = s_pre + E;                // [kRouteWaves][E] per-wave counts, then running bases
+    int32_t* s_off = s_run + kRouteWaves * E;  // [E] offsets
+    int32_t* s_w = s_off + E;                  // [kRouteWaves] scan scratch
+    const int tid = threadIdx.x, wv = tid / kWave, lane = tid % kWave;
+    const int64_t lo = (int64_t)b * kRouteThreads;
+    for (int e = tid; e < 6 * E; e += kRouteThreads) lds[e] = 0;
+    // this wave's slot (index and weight)
+    const int64_t f = lo + tid;
+    int my_e = -1;
+    float my_w = 0.f;
+    if (f < TK) {
+        const int64_t v = topk_idx[f];
+        if (v >= 0 && v < E) {
+            my_e = (int)v;
+            my_w = topk_w[f];
+        }
+    }
+    __syncthreads();
+    // every slot of the batch counted
+    int bad = 0;
+    for (int64_t g = tid; g < TK; g += kRouteThreads) {
+        const int64_t v = topk_idx[g];
+        if (v >= E) {
+            bad = 1;
+        } else if (v >= 0) {
+            atomicAdd(&s_tot[v], 1);
+            if (g < lo)
+                atomicAdd(&s_pre[v], 1);
+            else if (g < lo + kRouteThreads)
+                atomicAdd(&s_run[((g - lo) / kWave) * E + v], 1);
+        }
+    }
+    __syncthreads();
+    // offsets, and the running base of each wave: the expert's offset, its
+    // slots before this block, then the earlier waves of this block
+    const int ept = (E + kRouteThreads - 1) / kRouteThreads;
+    int my_tot = 0;
+    for (int j = 0; j < ept; ++j) {
+        const int e = ept * tid + j;
+        if (e < E) my_tot += s_tot[e];
+    }
+    int R = 0;
+    int off = block_exclusive_scan(my_tot, &R, s_w);
+    for (int j = 0; j < ept; ++j) {
+        const int e = ept * tid + j;
+        if (e >= E) continue;
+        s_off[e] = off;
+        int run = off + s_pre[e];
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) {
+            const int c = s_run[w * E + e];
+            s_run[w * E + e] = run;
+            run += c;
+        }
+        off += s_tot[e];
+    }
+    __syncthreads();
+    // the stable rank of the wave's slot: lanes holding the same expert find
+    // each other with one ballot per index bit, the lower lanes first
+    if (f - lane < TK) {  // wave-uniform: the wave's first slot exists
+        unsigned long long peers = __ballot(my_e >= 0);
+        for (int bt = 0; bt < nbits; ++bt) {
+            const int bit = (my_e >> bt) & 1;
+            const unsigned long long set = __ballot(bit);
+            peers &= bit ? set : ~set;
+        }
+        if (my_e >= 0) {
+            const int r = s_run[wv * E + my_e] + __popcll(peers & ((1ull << lane) - 1ull));
+            pool_src[r] = (int32_t)f;
+            slot_to_pool[f] = r;
+            pool_w[r] = my_w;
+            pool_tok[r] = (int32_t)(f / K);
+        } else if (f < TK) {
+            slot_to_pool[f] = -1;
+        }
+    }
+    if (b == 0) {
+        const int err = __syncthreads_or(bad);
+        route_write_tables(E, R, err, s_tot, s_off, s_w, counts, offsets, mtiles, num_mtiles, err_flag,
+                           mtiles64, num_mtiles64, dec_rows);
+    }
+}
+
 // The fused layer's first launch for batches of at most kRouteWaves *
-// kSegSlots slots: block 0 does all of a1-a3 (it is the only routing block,
-// so it counts its own slots and no block waits for another), the others
+// kSegSlots slots: blocks [0, nroute) route (route_small_block), the others
 // quantise the token rows token-major.  The pool rows' A-scale words need
 // every token's words, so they are not gathered here.
 __global__ __launch_bounds__(256) void k_quantise_route(
     const uint16_t* __restrict__ x, int64_t T, int H, int tpb, uint8_t* __restrict__ x_q,
     uint8_t* __restrict__ tok_s, const int64_t* __restrict__ topk_idx,
-    const float* __restrict__ topk_w, int64_t TK, int E, int nbits, int K,
+    const float* __restrict__ topk_w, int64_t TK, int E, int nbits, int K, int nroute,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, MTile* __restrict__ mtiles,
     int32_t* __restrict__ num_mtiles, int32_t* __restrict__ err_flag,
     int32_t* __restrict__ pool_src, int32_t* __restrict__ slot_to_pool, float* __restrict__ pool_w,
     int32_t* __restrict__ pool_tok, MTile* __restrict__ mtiles64, int32_t* __restrict__ num_mtiles64,
     int dec_rows) {
     extern __shared__ int32_t lds[];
-    if (blockIdx.x == 0)
-        route_block<true>(0, topk_idx, topk_w, TK, E, nbits, K, nullptr, nullptr, 1, counts, offsets,
-                          mtiles, num_mtiles, err_flag, pool_src, slot_to_pool, pool_w, pool_tok,
-                          nullptr, H / 128, 0, nullptr, mtiles64, num_mtiles64, dec_rows, lds);
+    if ((int)blockIdx.x < nroute)
+        route_small_block(blockIdx.x, topk_idx, topk_w, TK, E, nbits, K, counts, offsets, mtiles, num_mtiles,
+                          err_flag, pool_src, slot_to_pool, pool_w, pool_tok, mtiles64, num_mtiles64, dec_rows,
+                          lds);
     else
-        dispatch_fp8_block(x, T, H, 1, tpb, nullptr, x_q, nullptr, tok_s, blockIdx.x - 1);
+        dispatch_fp8_block(x, T, H, 1, tpb, nullptr, x_q, nullptr, tok_s, blockIdx.x - nroute);
 }
 
 // A-scale words of the pool rows in packed k-major order (the layout the L1
