@@ -277,18 +277,21 @@ def main():
     l2_flop = 2.0 * R * I * H
     l1_s = per_launch["gemm_l1"] * 1e-3
     l1_tflops = l1_flop / l1_s / 1e12
-    # L1 algorithmic bytes: W1 codes and scales of every expert that holds a
-    # routed row, the token rows' codes once, each routed row's A-scale words,
-    # its weight and token index, the e4m3 activations and their scales
-    experts_used = int(np.unique(inp["topk_idx"][inp["topk_idx"] >= 0]).size)
-    l1_bytes = (experts_used * 2 * I * (H // 2 + H // 32) + T * H + R * (H // 32 + 8)
-                + R * (I + I // 32))
-    l1_bound = "mfma" if l1_flop / PEAK_TFLOPS >= l1_bytes / PEAK_HBM_GBS * 1e3 else "hbm"
-    l1_gbs = l1_bytes / l1_s / 1e9
     # the library's GEMMs with 64-row tiles serve batches with at most 64
     # routed slots per expert on average
     l1_kernel = {"64": "gemm_l1_decode", "128": "gemm_l1_t128", "persistent": "gemm_l1"}.get(
         a.gemm_tiles, "gemm_l1_decode" if T * K <= 64 * E else "gemm_l1")
+    # L1 algorithmic bytes: W1 codes and scales of every expert that holds a
+    # routed row, the token rows' codes once, the A-scale words (by token in
+    # the 64-row-tile GEMM up to 1024 routed slots, else per routed row), each
+    # routed row's weight and token index, the e4m3 activations and their
+    # scales
+    experts_used = int(np.unique(inp["topk_idx"][inp["topk_idx"] >= 0]).size)
+    a_scale_rows = T if (l1_kernel == "gemm_l1_decode" and T * K <= 1024) else R
+    l1_bytes = (experts_used * 2 * I * (H // 2 + H // 32) + T * H + a_scale_rows * (H // 32) + R * 8
+                + R * (I + I // 32))
+    l1_bound = "mfma" if l1_flop / PEAK_TFLOPS >= l1_bytes / PEAK_HBM_GBS * 1e3 else "hbm"
+    l1_gbs = l1_bytes / l1_s / 1e9
     l2_tflops = l2_flop / (per_launch["gemm_l2"] * 1e-3) / 1e12
     # algorithmic bytes of the bandwidth-bound kernels (see the design notes):
     # dispatch = x read, token-major codes and scale words written, topk_idx
