@@ -64,7 +64,7 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="also capture one moe_fused_forward_packed step into a HIP graph and report the replayed step "
                         "time (ms_per_step_graph) beside the main number")
-    p.add_argument("--gemm-tiles", choices=("auto", "persistent", "64", "128"), default="auto",
+    p.add_argument("--gemm-tiles", choices=("auto", "persistent", "64", "128", "fused"), default="auto",
                    help="which grouped-GEMM kernels the layer runs (moe_options_t.gemm_tiles); "
                         "auto: the library's choice by shape")
     p.add_argument("--copy-mib", type=int, default=0,
@@ -155,7 +155,8 @@ def main():
     moe.moe_pack_weights(d["W1q"], d["S1"], d["W2q"], d["S2"], prepacked, E=E, H=H, I=I, stream=stream)
 
     opts = moe.options(gemm_tiles={"auto": moe.MOE_TILES_AUTO, "persistent": moe.MOE_TILES_PERSISTENT,
-                                   "64": moe.MOE_TILES_64, "128": moe.MOE_TILES_128}[a.gemm_tiles])
+                                   "64": moe.MOE_TILES_64, "128": moe.MOE_TILES_128,
+                                   "fused": moe.MOE_TILES_FUSED}[a.gemm_tiles])
 
     def call(mode, st):
         if mode == "prepacked":
@@ -290,9 +291,17 @@ def main():
     a_scale_rows = T if (l1_kernel == "gemm_l1_decode" and T * K <= 1024) else R
     l1_bytes = (experts_used * 2 * I * (H // 2 + H // 32) + T * H + a_scale_rows * (H // 32) + R * 8
                 + R * (I + I // 32))
+    if a.gemm_tiles == "fused":
+        # L1 and L2 in one launch (the L2 stage is empty): both GEMMs' FLOP;
+        # bytes = both weights of the experts in use, the token codes, the
+        # A-scale words, weights and token indices, the bf16 L2 rows written
+        l1_kernel = "gemm_fused"
+        l1_flop = l1_flop + l2_flop
+        l1_bytes = (experts_used * 3 * I * (H // 2 + H // 32) + T * H + R * (H // 32 + 8) + R * H * 2)
+        l1_tflops = l1_flop / l1_s / 1e12
     l1_bound = "mfma" if l1_flop / PEAK_TFLOPS >= l1_bytes / PEAK_HBM_GBS * 1e3 else "hbm"
     l1_gbs = l1_bytes / l1_s / 1e9
-    l2_tflops = l2_flop / (per_launch["gemm_l2"] * 1e-3) / 1e12
+    l2_tflops = None if a.gemm_tiles == "fused" else l2_flop / (per_launch["gemm_l2"] * 1e-3) / 1e12
     # algorithmic bytes of the bandwidth-bound kernels (see the design notes):
     # dispatch = x read, token-major codes and scale words written, topk_idx
     # read by the histogram in the same launch; pool scales = the pool rows'
@@ -301,7 +310,7 @@ def main():
     pool_s_bytes = 2 * R * (H // 32) + 4 * R
     comb_bytes = R * H * 2 + T * H * 2 + T * K * 4
 
-    traffic = measured_traffic(a.workload)
+    traffic = None if a.gemm_tiles == "fused" else measured_traffic(a.workload)
     roofline = {"bound": l1_bound, "kernel": l1_kernel}
     if l1_bound == "mfma":
         roofline.update(achieved=round(l1_tflops, 2), peak=PEAK_TFLOPS, unit="TFLOP/s",
@@ -343,7 +352,7 @@ def main():
         "kernels_ms_per_launch": {k: round(v, 4) for k, v in per_launch.items()},
         "ms_per_step_with_kernel_events": round(ms_per_step_events, 4),
         "kernels": {
-            "gemm_l2_tflops": round(l2_tflops, 2),
+            "gemm_l2_tflops": None if l2_tflops is None else round(l2_tflops, 2),
             "dispatch_gbs": round(disp_bytes / (per_launch["dispatch"] * 1e-3) / 1e9, 1),
             "pool_scales_gbs": round(pool_s_bytes / (per_launch["pool_scales"] * 1e-3) / 1e9, 1),
             "combine_gbs": round(comb_bytes / (per_launch["combine"] * 1e-3) / 1e9, 1),

@@ -33,6 +33,7 @@ MOE_TILES_AUTO = 0
 MOE_TILES_PERSISTENT = 1
 MOE_TILES_64 = 2
 MOE_TILES_128 = 3
+MOE_TILES_FUSED = 4
 
 EXPORTED = ("moe_default_options", "moe_workspace_bytes", "moe_dispatch_workspace_bytes",
             "moe_fused_forward", "moe_dispatch", "moe_combine", "moe_workspace_views",

@@ -196,19 +196,22 @@ bool route_fused(const Layout& L, int E) { return (int64_t)route_blocks(L) * E <
 // routed slots per expert on average: the weights stream through once);
 // rm = 2: 128-row tiles for l1 / l2 where set.  The tile-per-workgroup
 // kernels read the second tile table, which the one-launch routing writes.
+// fused: L1 and L2 in one launch over the 128-row table (rm = 2).
 struct TilePlan {
     int rm;
     bool l1, l2;
+    bool fused;
 };
 constexpr bool kT128L1 = false, kT128L2 = false;
 TilePlan tile_plan(const moe_shape_t* s, const Layout& L, int choice) {
     const int64_t TK = (int64_t)s->T * s->K;
-    if (choice == MOE_TILES_PERSISTENT || !route_fused(L, s->E)) return {0, false, false};
-    if (choice == MOE_TILES_64) return {1, true, true};
-    if (choice == MOE_TILES_128) return {2, true, true};
-    if (TK <= (int64_t)kDecRows * s->E) return {1, true, true};
-    if (kT128L1 || kT128L2) return {2, kT128L1, kT128L2};
-    return {0, false, false};
+    if (choice == MOE_TILES_PERSISTENT || !route_fused(L, s->E)) return {0, false, false, false};
+    if (choice == MOE_TILES_64) return {1, true, true, false};
+    if (choice == MOE_TILES_128) return {2, true, true, false};
+    if (choice == MOE_TILES_FUSED) return {kFusedRows / kDecRows, true, true, true};
+    if (TK <= (int64_t)kDecRows * s->E) return {1, true, true, false};
+    if (kT128L1 || kT128L2) return {2, kT128L1, kT128L2, false};
+    return {0, false, false, false};
 }
 
 // a1 (unless the caller's first launch already counted: `counted`), a2, a3,
@@ -382,7 +385,7 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     if (!shape_basic_ok(s)) return MOE_ERR_INVALID_ARG;
     const moe_options_t o = opt ? *opt : moe_default_options();
     if (!isnan(o.activation_clamp)) return MOE_ERR_UNSUPPORTED;
-    if (o.gemm_tiles < MOE_TILES_AUTO || o.gemm_tiles > MOE_TILES_128) return MOE_ERR_INVALID_ARG;
+    if (o.gemm_tiles < MOE_TILES_AUTO || o.gemm_tiles > MOE_TILES_FUSED) return MOE_ERR_INVALID_ARG;
     if (!fused_shape_ok(s)) return MOE_ERR_UNSUPPORTED;
     if (s->T == 0) return MOE_OK;
     if (!x || !topk_idx || !topk_w || !W1q || !W2q || !y) return MOE_ERR_INVALID_ARG;
@@ -394,8 +397,10 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
             return MOE_ERR_INVALID_ARG;  // scale rows are read as 4-byte words
     }
     const Layout L = make_layout(s);
-    if ((o.gemm_tiles == MOE_TILES_64 || o.gemm_tiles == MOE_TILES_128) && !route_fused(L, s->E))
+    if ((o.gemm_tiles == MOE_TILES_64 || o.gemm_tiles == MOE_TILES_128 || o.gemm_tiles == MOE_TILES_FUSED) &&
+        !route_fused(L, s->E))
         return MOE_ERR_UNSUPPORTED;
+    if (o.gemm_tiles == MOE_TILES_FUSED && s->I > kFusedMaxI) return MOE_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
         return MOE_ERR_WORKSPACE;
     if (!device_ok()) return MOE_ERR_DEVICE;
@@ -506,7 +511,20 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     g1.act_s = act_s;
     g1.I = I;
     g1.fast_math = o.fast_math ? 1 : 0;
-    if (plan.l1) {
+    if (plan.fused) {
+        // both GEMMs in one launch, the activations kept in LDS
+        g1.mtiles = reinterpret_cast<const MTile*>(ws + L.mtiles64);
+        g1.num_mtiles = reinterpret_cast<const int32_t*>(ws + L.num_mtiles64);
+        GemmArgs g2 = g1;
+        g2.B = W2q;
+        g2.SB = s2t;
+        g2.Kdim = I;
+        g2.N = H;
+        g2.ntiles = H / kBN;
+        g2.out = l2_out;
+        hipLaunchKernelGGL(k_gemm_fused, dim3((dec_grid_rows + 7u) / 8u * 8u), dim3(kGemmThreads), 0, stream,
+                           g1, g2);
+    } else if (plan.l1) {
         if (sa_by_token) {
             g1.SA = tok_s;  // token-major words [T][H/128]
             g1.sa_step = 4;
@@ -522,28 +540,30 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
     }
     prof_mark(pc, MOE_STAGE_GEMM_L1, stream);
 
-    GemmArgs g2 = g1;
-    g2.A = act_q;
-    g2.SA = act_s;
-    g2.sa_step = 4 * L.cap;  // packed k-major words of the pool rows
-    g2.sa_by_token = 0;
-    g2.pool_tok = nullptr;
-    g2.B = W2q;
-    g2.SB = s2t;
-    g2.Kdim = I;
-    g2.N = H;
-    g2.ntiles = H / kBN;
-    g2.out = l2_out;
-    if (plan.l2) {
-        g2.mtiles = reinterpret_cast<const MTile*>(ws + L.mtiles64);
-        g2.num_mtiles = reinterpret_cast<const int32_t*>(ws + L.num_mtiles64);
-        hipLaunchKernelGGL(plan.rm == 1 ? k_gemm_l2_decode : k_gemm_l2_t128,
-                           dim3(dec_grid_rows * (unsigned)g2.ntiles), dim3(kGemmThreads), 0, stream, g2);
-    } else {
-        g2.mtiles = reinterpret_cast<const MTile*>(ws + L.mtiles);
-        g2.num_mtiles = reinterpret_cast<const int32_t*>(ws + L.num_mtiles);
-        hipLaunchKernelGGL(k_gemm_l2, dim3(gemm_grid(L.max_mtiles * g2.ntiles)), dim3(kGemmThreads), 0,
-                           stream, g2);
+    if (!plan.fused) {
+        GemmArgs g2 = g1;
+        g2.A = act_q;
+        g2.SA = act_s;
+        g2.sa_step = 4 * L.cap;  // packed k-major words of the pool rows
+        g2.sa_by_token = 0;
+        g2.pool_tok = nullptr;
+        g2.B = W2q;
+        g2.SB = s2t;
+        g2.Kdim = I;
+        g2.N = H;
+        g2.ntiles = H / kBN;
+        g2.out = l2_out;
+        if (plan.l2) {
+            g2.mtiles = reinterpret_cast<const MTile*>(ws + L.mtiles64);
+            g2.num_mtiles = reinterpret_cast<const int32_t*>(ws + L.num_mtiles64);
+            hipLaunchKernelGGL(plan.rm == 1 ? k_gemm_l2_decode : k_gemm_l2_t128,
+                               dim3(dec_grid_rows * (unsigned)g2.ntiles), dim3(kGemmThreads), 0, stream, g2);
+        } else {
+            g2.mtiles = reinterpret_cast<const MTile*>(ws + L.mtiles);
+            g2.num_mtiles = reinterpret_cast<const int32_t*>(ws + L.num_mtiles);
+            hipLaunchKernelGGL(k_gemm_l2, dim3(gemm_grid(L.max_mtiles * g2.ntiles)), dim3(kGemmThreads), 0,
+                               stream, g2);
+        }
     }
     prof_mark(pc, MOE_STAGE_GEMM_L2, stream);
 

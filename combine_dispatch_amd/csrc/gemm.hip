@@ -1409,6 +1409,498 @@ __device__ __forceinline__ void gemm_decode(const GemmArgs& g, uint8_t* lds, flo
     }
 }
 
+
+// ---- L1 and L2 in one launch, the activations kept in LDS -----------------
+// One workgroup per m-tile of at most kFusedRows rows of one expert (the
+// second tile table).  First L1 over all 2I gate/up columns in I/128 chunks of
+// 256 LDS B rows (gate and up of four quantisation groups, the narrow column
+// order: wave w takes gate and up of group w), each chunk's SwiGLU / requant
+// epilogue writing its 128 e4m3 activation columns -- exactly one 128-wide K
+// block of L2 -- and their scale bytes into LDS; then L2 over all H output
+// columns in H/256 chunks, its A operand read from that LDS tile, each
+// chunk's bf16 rows stored to the pool-order output.  Every wave covers all
+// rows (four 32-row MFMA tiles; those without rows skip their MFMAs) and two
+// 32-column tiles, so every output gets the same MFMAs in the same K order as
+// in the other GEMM kernels, hence the same bits.
+//
+// K steps of 64 (one MFMA sub-step): three LDS stages of 16 KiB (A 128 rows x
+// 64 B, B 256 rows x 32 B) filled by direct loads two steps ahead, the stream
+// running on across chunk and phase boundaries; the scale words of each
+// 128-wide K block (each wave's copy of the A rows' words, and the B words)
+// go to a ring of two slots with the block's first step.  Per wave and step:
+// L1 7 loads on a block's first step and 4 on its second, L2 3 and 2; an L2
+// chunk's epilogue issues kFusedStores stores.  The waits count them, taking
+// vector memory operations to complete in issue order.
+//
+// Measured on one MI355X with T = 16384, H = 2048, I = 768, E = 128, K = 8:
+// 1.12 ms for this launch against 0.58 ms for the two separate GEMMs.  The
+// 99 KB activation tile leaves room in the 160 KiB LDS for 16 KiB stages
+// only, so a barrier covers 8 MFMAs per wave (32 in the persistent GEMMs),
+// and with one wave per SIMD the LDS reads, scalar work and barriers of each
+// step are not hidden (1.5 k cycles per step of 512 MFMA cycles even with the
+// loads taken out).  The layer offers it as a choice (gemm_tiles), not by
+// default.
+constexpr int kFStageA = kFusedRows * 64;
+constexpr int kFStageB = kBN * 32;
+constexpr int kFStage = kFStageA + kFStageB;
+constexpr int kFScaleSA = 4 * kFusedRows * 4;
+constexpr int kFScale = kFScaleSA + kBN * 4;
+constexpr int kFusedStores = 32;
+constexpr int kFusedLds = 3 * kFStage + 2 * kFScale + kFusedRows * kFusedMaxI + (kFusedMaxI / 128) * kFusedRows * 4 +
+                          kFusedRows * 4;
+static_assert(kFusedLds <= 160 * 1024, "LDS");
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) and a workgroup barrier.
+template <int N>
+__device__ __forceinline__ void waitcnt_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void gemm_fused(const GemmArgs& g1, const GemmArgs& g2, uint8_t* lds) {
+    // the arguments in scalars: the loop must not read them through a
+    // pointer (a generic load there waits for every direct load in flight)
+    const uint8_t* const A1 = g1.A;
+    const uint8_t* const SA1 = g1.SA;
+    const uint8_t* const B1 = g1.B;
+    const uint8_t* const SB1 = g1.SB;
+    const uint8_t* const B2 = g2.B;
+    const uint8_t* const SB2 = g2.SB;
+    uint16_t* const OUT = g2.out;
+    const int64_t sa_step1 = g1.sa_step;
+    const int32_t* const pool_tok = g1.pool_tok;
+    const float* const pool_w = g1.pool_w;
+    const MTile* const mtiles = g1.mtiles;
+    const int32_t* const num_mtiles = g1.num_mtiles;
+    const int T1 = g1.T, N1 = g1.N, N2 = g2.N, ntl1 = g1.ntiles, ntl2 = g2.ntiles;
+    const bool tiled1 = g1.b_tiled != 0, tiled2 = g2.b_tiled != 0, fast_math = g1.fast_math != 0;
+    uint8_t* stg = lds;                                  // 3 stages
+    uint8_t* scl = stg + 3 * kFStage;                    // 2 scale slots
+    uint8_t* act = scl + 2 * kFScale;                    // [rows][I] e4m3, swizzled
+    uint8_t* sact = act + kFusedRows * kFusedMaxI;       // words [I/128][rows]
+    float* s_w = reinterpret_cast<float*>(sact + (kFusedMaxI / 128) * kFusedRows * 4);
+
+    const int tid = threadIdx.x;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int hs = 16 * h;
+
+    // XCD-contiguous tiles: the hardware places workgroup b on XCD b % 8 and
+    // XCD x takes the tiles [total*x/8, total*(x+1)/8), so the tiles of an
+    // expert mostly run together on one XCD and share its weights through
+    // that XCD's L2.  (The grid is a multiple of 8, at least 8 times the
+    // largest share; the extra workgroups return.)
+    const int total = *num_mtiles;
+    const int xcd = (int)blockIdx.x & 7;
+    const int tile = (int)((int64_t)total * xcd / 8) + ((int)blockIdx.x >> 3);
+    if (tile >= (int)((int64_t)total * (xcd + 1) / 8)) return;
+    const MTile rec = mtiles[tile];
+    const int e = __builtin_amdgcn_readfirstlane(rec.expert);
+    const int row0 = __builtin_amdgcn_readfirstlane(rec.row0);
+    const int nrows = __builtin_amdgcn_readfirstlane(rec.nrows);
+    const int nrt = (nrows + 31) >> 5;  // 32-row MFMA tiles holding rows
+
+    const int H = g1.Kdim, I = g1.I;
+    const int nkb1 = H / 128, nkb2 = I / 128;  // 128-wide K blocks per chunk
+    const int nch1 = I / 128, nch2 = H / kBN;  // chunks
+    const int S1 = 2 * nkb1 * nch1;            // K steps of the L1 phase
+    const int ST = S1 + 2 * nkb2 * nch2;
+
+    // ---- per-lane load offsets ---------------------------------------------
+    // A (L1): chunk q = tid + 256 p (p = 0, 1) is LDS row q/4, physical chunk
+    // q%4 holding logical chunk (q%4) ^ ((row/4)%4), from the token row
+    // pool_tok[row0 + row] (clamped into the buffer).
+    uint32_t a_off0, a_off1;
+    {
+        const uint32_t tmax = (uint32_t)(T1 - 1);
+        const int lch = (tid & 3) ^ ((tid >> 4) & 3);
+        const uint32_t t0 = min((uint32_t)pool_tok[row0 + (tid >> 2)], tmax);
+        const uint32_t t1 = min((uint32_t)pool_tok[row0 + (tid >> 2) + 64], tmax);
+        a_off0 = t0 * (uint32_t)H + 16u * (uint32_t)lch;
+        a_off1 = t1 * (uint32_t)H + 16u * (uint32_t)lch;
+    }
+    // B: chunk q = tid + 256 p is LDS row q/2 (weight row b_row_narrow of it),
+    // physical chunk q%2 holding logical (q%2) ^ ((row/8)%2), 32 bytes a row
+    // per step.
+    auto boffs = [&](auto mode, bool tiled, int kdim, int Iv, uint32_t& o0, uint32_t& o1) __attribute__((always_inline)) {
+        constexpr int MODE = decltype(mode)::value;
+        const int rs = tiled ? kBK / 2 : kdim / 2, bI = tiled ? 128 : Iv;
+        const int lch = (tid & 1) ^ ((tid >> 4) & 1);
+        const int r0 = tid >> 1, r1 = r0 + 128;
+        o0 = (uint32_t)((b_row_narrow<MODE>(0, r0, bI) - b_row_narrow<MODE>(0, 0, bI)) * rs + 16 * lch);
+        o1 = (uint32_t)((b_row_narrow<MODE>(0, r1, bI) - b_row_narrow<MODE>(0, 0, bI)) * rs + 16 * lch);
+    };
+    uint32_t b1_o0, b1_o1, b2_o0, b2_o1;
+    boffs(std::integral_constant<int, kL1>{}, tiled1, H, I, b1_o0, b1_o1);
+    boffs(std::integral_constant<int, kL2>{}, tiled2, I, I, b2_o0, b2_o1);
+    // B scale words: LDS word tid holds the word of LDS B row tid
+    const uint32_t sb1_off = (uint32_t)(4 * (b_row_narrow<kL1>(0, tid, I) - b_row_narrow<kL1>(0, 0, I)));
+    const uint32_t sb2_off = (uint32_t)(4 * (b_row_narrow<kL2>(0, tid, H) - b_row_narrow<kL2>(0, 0, H)));
+    const int64_t b1_ks = tiled1 ? (int64_t)kBTileBytes : kBK / 2;
+    const int64_t b2_ks = tiled2 ? (int64_t)kBTileBytes : kBK / 2;
+    // scalar bases of chunk c
+    auto b1_base = [&](int c) __attribute__((always_inline)) {
+        return tiled1 ? B1 + ((int64_t)e * ntl1 + c) * (int64_t)nkb1 * kBTileBytes
+                          : B1 + ((int64_t)e * N1 + b_row_narrow<kL1>(c, 0, I)) * (H / 2);
+    };
+    auto b2_base = [&](int c) __attribute__((always_inline)) {
+        return tiled2 ? B2 + ((int64_t)e * ntl2 + c) * (int64_t)nkb2 * kBTileBytes
+                          : B2 + ((int64_t)e * N2 + b_row_narrow<kL2>(c, 0, H)) * (I / 2);
+    };
+    auto sb1_base = [&](int c) __attribute__((always_inline)) {
+        return SB1 + (int64_t)e * nkb1 * ((int64_t)N1 * 4) + (int64_t)b_row_narrow<kL1>(c, 0, I) * 4;
+    };
+    auto sb2_base = [&](int c) __attribute__((always_inline)) {
+        return SB2 + (int64_t)e * nkb2 * ((int64_t)N2 * 4) + (int64_t)b_row_narrow<kL2>(c, 0, H) * 4;
+    };
+    const uint8_t* sa_base = SA1 + (int64_t)row0 * 4;
+
+    if (tid < kFusedRows) s_w[tid] = pool_w[row0 + tid];  // rows past the tile: unused
+
+    // ---- loads, in a cursor advanced per step ----------------------------
+    // Running scalar pointers of the next step to load (A rows, B rows, A
+    // and B scale words of its K block), moved by constant strides and set
+    // afresh only at a chunk's end.
+    int lu = 0, lc = 0, lissued = 0;  // step inside the chunk, chunk, steps loaded
+    bool lp2 = false;                  // the next step to load is in the L2 phase
+    const uint8_t *la = A1, *lb = nullptr, *lsa = sa_base, *lsb = nullptr;
+    const int64_t sb1_step = (int64_t)N1 * 4, sb2_step = (int64_t)N2 * 4;
+    auto set_chunk = [&]() __attribute__((always_inline)) {
+        if (!lp2) {
+            la = A1;
+            lsa = sa_base;
+            lb = b1_base(lc);
+            lsb = sb1_base(lc);
+        } else {
+            lb = b2_base(lc);
+            lsb = sb2_base(lc);
+        }
+    };
+    set_chunk();
+    const uint32_t stg0 = lds_addr(stg), scl0 = lds_addr(scl);
+    uint32_t lst = stg0;   // stage of the next load
+    uint32_t lsc = scl0;   // scale slot of its K block
+    auto issue_next = [&]() __attribute__((always_inline)) {
+        const uint32_t wa = lst + 1024u * wid, wb = lst + kFStageA + 1024u * wid;
+        const bool first = (lu & 1) == 0;  // the K block's first step: its scale words
+        if (!lp2) {
+            dma_x4(wa, la, a_off0);
+            dma_x4(wa + 4096, la, a_off1);
+            dma_x4(wb, lb, b1_o0);
+            dma_x4(wb + 4096, lb, b1_o1);
+            if (first) {
+                dma_x1(lsc + 512u * wid, lsa, 4u * lane);
+                dma_x1(lsc + 512u * wid + 256u, lsa, 4u * lane + 256u);
+                dma_x1(lsc + kFScaleSA + 256u * wid, lsb, sb1_off);
+            }
+        } else {
+            dma_x4(wb, lb, b2_o0);
+            dma_x4(wb + 4096, lb, b2_o1);
+            if (first) dma_x1(lsc + kFScaleSA + 256u * wid, lsb, sb2_off);
+        }
+        ++lissued;
+        lst = lst == stg0 + 2 * kFStage ? stg0 : lst + kFStage;
+        if (!first) lsc = lsc == scl0 ? scl0 + kFScale : scl0;  // the block's last step
+        if (++lu == 2 * (lp2 ? nkb2 : nkb1)) {
+            lu = 0;
+            if (!lp2) {
+                if (++lc == nch1) lc = 0, lp2 = true;
+            } else {
+                ++lc;
+            }
+            if (lissued < ST) set_chunk();
+        } else if (first) {
+            la += 64;
+            lb += 32;
+        } else {
+            la += 64;
+            lb += (lp2 ? b2_ks : b1_ks) - 32;
+            lsa += sa_step1;
+            lsb += lp2 ? sb2_step : sb1_step;
+        }
+    };
+
+    v16f acc[4][2];
+    auto clear = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    };
+    clear();
+
+    // MFMA operands of one K step for one wave: its four row tiles' A
+    // fragments and scale words, its two column tiles' B fragments and words.
+    struct Frags {
+        v8i a[4];
+        v4i b[2];
+        int wa[4], wb[2];
+    };
+    Frags fa, fb;  // even and odd steps
+    const int b_sw = (l32 >> 3) & 1;  // B rows: (row/8)%2 of rows 32 j + l32
+    const int a_sw = (l32 >> 2) & 3;  // A stage rows: (row/4)%4
+    // activation tile: element (row, column) at row * I + 128 * kb' +
+    // 16 * (q ^ (row/2)%8) + column % 16, with K block kb = column / 128 (kb' =
+    // kb ^ (row%2) when I/128 is even, else kb, so that rows of either parity
+    // start in different halves of the banks) and chunk q = (column % 128) / 16
+    const bool kb_swap = (nkb2 & 1) == 0;
+    const int act_sw = (l32 >> 1) & 7;
+
+    // Reads of step t's operands, in pieces: piece 0 the B fragments and
+    // words, piece 1 + i row tile i (skipped without rows unless FULL).  L1
+    // takes A from the stage (columns wid, wid + 4: gate and up of group
+    // wid); L2 takes A from the activation tile at K block m, sub-step S
+    // (columns 2 wid, 2 wid + 1).
+    auto read_piece = [&](Frags& f, int p, bool l2, const uint8_t* sA, const uint8_t* sc, int m, int S, auto full)
+        __attribute__((always_inline)) {
+        const int jn0 = l2 ? 2 * wid : wid, jn1 = l2 ? 2 * wid + 1 : wid + 4;
+        if (p == 0) {
+            const uint8_t* sB = sA + kFStageA;
+            const uint4 v0 = *reinterpret_cast<const uint4*>(sB + (32 * jn0 + l32) * 32 + 16 * (h ^ b_sw));
+            const uint4 v1 = *reinterpret_cast<const uint4*>(sB + (32 * jn1 + l32) * 32 + 16 * (h ^ b_sw));
+            f.b[0] = v4i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w};
+            f.b[1] = v4i{(int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+            f.wb[0] = (int)(*reinterpret_cast<const uint32_t*>(sc + kFScaleSA + 4 * (32 * jn0 + l32)) >> hs);
+            f.wb[1] = (int)(*reinterpret_cast<const uint32_t*>(sc + kFScaleSA + 4 * (32 * jn1 + l32)) >> hs);
+            return;
+        }
+        const int i = p - 1;
+        if (!decltype(full)::value && i >= nrt) return;
+        uint4 v0, v1;
+        if (!l2) {
+            const uint8_t* rowp = sA + (32 * i + l32) * 64;
+            v0 = *reinterpret_cast<const uint4*>(rowp + 16 * (h ^ a_sw));
+            v1 = *reinterpret_cast<const uint4*>(rowp + 16 * ((2 + h) ^ a_sw));
+            f.wa[i] = (int)(*reinterpret_cast<const uint32_t*>(sc + 512 * wid + 4 * (32 * i + l32)) >> hs);
+        } else {
+            const int kb = kb_swap ? (m ^ (l32 & 1)) : m;
+            const uint8_t* rowp = act + (32 * i + l32) * I + 128 * kb;
+            v0 = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * S + h) ^ act_sw));
+            v1 = *reinterpret_cast<const uint4*>(rowp + 16 * ((4 * S + 2 + h) ^ act_sw));
+            f.wa[i] = (int)(reinterpret_cast<const uint32_t*>(sact)[m * kFusedRows + 32 * i + l32] >> hs);
+        }
+        f.a[i] = v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+    };
+    // the MFMAs of row tile i of a step whose operands f holds (sub-step S)
+    auto mfma_tile = [&](const Frags& f, int i, auto sconst, auto full) __attribute__((always_inline)) {
+        constexpr int S = decltype(sconst)::value;
+        if (!decltype(full)::value && i >= nrt) return;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const v8i b = v8i{f.b[j][0], f.b[j][1], f.b[j][2], f.b[j][3], 0, 0, 0, 0};
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], b, acc[i][j], 0, 4, S, f.wa[i], S,
+                                                                        f.wb[j]);
+        }
+    };
+
+    // L1 chunk c's epilogue: gate/up to bf16, silu(gate) * up * w, per-32
+    // amax, UE8M0, e4m3 codes and scale bytes into the activation tile (the
+    // same arithmetic as the other L1 epilogues).
+    const int gbyte = ((wid & 1) << 1) | (wid >> 1);  // group wid in the word's byte order
+    const uint32_t bshift = 8u * (uint32_t)(l32 & 3);
+    auto epilogue_l1 = [&](int c, auto full) __attribute__((always_inline)) {
+        const int q = 2 * wid + (l32 >> 4), byte = l32 & 15;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (!decltype(full)::value && i >= nrt) continue;
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int lrow0 = 32 * i + 8 * rq + 4 * h;
+                float gt[4], up[4], a[4];
+                uint32_t mx[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const uint32_t gu = pack_bf16x2(acc[i][0][4 * rq + rr], acc[i][1][4 * rq + rr]);
+                    gt[rr] = bf16_lo(gu);
+                    up[rr] = bf16_hi(gu);
+                }
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const float wr = s_w[lrow0 + rr];
+                    if (fast_math) {
+                        const float ex = __builtin_amdgcn_exp2f(-gt[rr] * 1.4426950408889634f);
+                        a[rr] = ((gt[rr] * __builtin_amdgcn_rcpf(1.0f + ex)) * up[rr]) * wr;
+                    } else {
+                        a[rr] = ((gt[rr] / (1.0f + expf(-gt[rr]))) * up[rr]) * wr;
+                    }
+                    mx[rr] = __float_as_uint(fabsf(a[rr]));
+                }
+                group32_max_u32x4(mx);
+                uint32_t b[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int row = lrow0 + rr;
+                    b[rr] = ue8m0_e4m3_bits(mx[rr]);
+                    const uint32_t code = pack_fp8x2_scaled(a[rr], 0.f, b[rr]);
+                    const int kb = kb_swap ? (c ^ (row & 1)) : c;
+                    act[row * I + 128 * kb + 16 * (q ^ ((row >> 1) & 7)) + byte] = (uint8_t)code;
+                }
+                // lanes l32 = 0..3 write the scale byte of rows lrow0 + l32
+                const uint32_t b4 = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+                if (l32 < 4) sact[4 * (c * kFusedRows + lrow0 + l32) + gbyte] = (uint8_t)(b4 >> bshift);
+            }
+        }
+    };
+    // L2 chunk c's epilogue: bf16 rows.  A lane holds two adjacent columns of
+    // 16 rows per row tile; neighbouring lanes trade one of each pair of rows
+    // (DPP lane ^ 1) so that each stores four adjacent columns (8 bytes) of
+    // one row: kFusedStores stores per lane, rows past the tile's end dropped
+    // by the buffer range.
+    auto epilogue_l2 = [&](int c) __attribute__((always_inline)) {
+        const int N = H;
+        uint8_t* out_base = reinterpret_cast<uint8_t*>(OUT + (int64_t)row0 * N + c * kBN);
+        const __amdgpu_buffer_rsrc_t out_rs = rows_rsrc(out_base, nrows * N * 2);
+        const bool odd = (l32 & 1) != 0;
+        const int col = 64 * wid + 2 * (l32 & ~1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const int lrow = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                const uint32_t v0 = pack_bf16x2(acc[i][0][r], acc[i][1][r]);          // row lrow
+                const uint32_t v1 = pack_bf16x2(acc[i][0][r + 1], acc[i][1][r + 1]);  // row lrow + 1
+                const uint32_t got = dpp_u32<kDppQuadSwap1>(odd ? v0 : v1);
+                const v2i w = odd ? v2i{(int)got, (int)v1} : v2i{(int)v0, (int)got};
+                const int row = lrow + (odd ? 1 : 0);
+                __builtin_amdgcn_raw_buffer_store_b64(w, out_rs, 2 * (row * N + col), 0, kStoreDecode);
+            }
+        }
+    };
+
+    // ---- the step stream ---------------------------------------------------
+    // Iteration t: wait for step t's loads (and every wave's reads of step
+    // t-1's stage), load step t+2 into that stage, then step t-1's MFMAs with
+    // step t's operand reads between them; a chunk's epilogue follows its last
+    // MFMAs (in the iteration of the next chunk's first step, always even).
+    // The newer vector memory operations at the wait: step t+1's loads (L1:
+    // 7 on a K block's first step, 4 on its second; L2: 3 and 2) and the
+    // stores of an L2 epilogue in either of the two previous iterations.
+    issue_next();
+    issue_next();
+    auto stream = [&](auto full) __attribute__((always_inline)) {
+        int t = 0;
+        const uint8_t* sst = stg;  // stage of step t
+        const uint8_t* rsc = scl;  // scale slot of its K block
+        bool e1 = false, e2 = false;  // stores issued in iteration t-1, t-2
+        const std::integral_constant<int, 0> s0;
+        const std::integral_constant<int, 1> s1;
+        auto begin = [&](auto ncst) __attribute__((always_inline)) {
+            constexpr int N = decltype(ncst)::value;
+            waitcnt_barrier<N>();
+            if (lissued < ST) issue_next();
+        };
+        auto begin_l2 = [&](auto ncst) __attribute__((always_inline)) {
+            constexpr int N = decltype(ncst)::value;
+            if (e1 || e2)
+                waitcnt_barrier<N + kFusedStores>();
+            else
+                waitcnt_barrier<N>();
+            e2 = e1;
+            e1 = false;
+            if (lissued < ST) issue_next();
+        };
+        auto adv = [&](bool block_end) __attribute__((always_inline)) {
+            ++t;
+            sst = sst == stg + 2 * kFStage ? stg : sst + kFStage;
+            if (block_end) rsc = rsc == scl ? scl + kFScale : scl;
+        };
+        // step t-1's MFMAs (operands in fm, sub-step SM) with step t's reads
+        // into fr (phase l2, K block m of the chunk, sub-step SR)
+        auto overlap = [&](Frags& fr, Frags& fm, bool l2, int m, auto sr, auto sm) __attribute__((always_inline)) {
+            constexpr int SR = decltype(sr)::value;
+            read_piece(fr, 0, l2, sst, rsc, m, SR, full);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                mfma_tile(fm, i, sm, full);
+                read_piece(fr, 1 + i, l2, sst, rsc, m, SR, full);
+            }
+        };
+        const std::integral_constant<int, 7> n7;
+        const std::integral_constant<int, 4> n4;
+        const std::integral_constant<int, 3> n3;
+        const std::integral_constant<int, 2> n2;
+        const std::integral_constant<int, 0> n0;
+        // the second step of an L1 K block (waits as its successor: the next
+        // block's first step, or L2's at the phase end)
+        auto l1_odd = [&](int m) __attribute__((always_inline)) {
+            if (t + 1 == S1) begin(n3); else begin(n7);
+            overlap(fb, fa, false, m, s1, s0);
+            adv(true);
+        };
+        auto l2_odd = [&](int m) __attribute__((always_inline)) {
+            if (t + 1 == ST) begin_l2(n0); else begin_l2(n3);
+            overlap(fb, fa, true, m, s1, s0);
+            adv(true);
+        };
+        auto l1_rest = [&]() __attribute__((always_inline)) {
+            for (int m = 1; m < nkb1; ++m) {
+                begin(n4);
+                overlap(fa, fb, false, m, s0, s1);
+                adv(false);
+                l1_odd(m);
+            }
+        };
+        auto l2_rest = [&]() __attribute__((always_inline)) {
+            for (int m = 1; m < nkb2; ++m) {
+                begin_l2(n2);
+                overlap(fa, fb, true, m, s0, s1);
+                adv(false);
+                l2_odd(m);
+            }
+        };
+        // L1 phase: chunk 0 starts the stream
+        begin(n4);
+#pragma unroll
+        for (int p = 0; p < 5; ++p) read_piece(fa, p, false, sst, rsc, 0, 0, full);
+        adv(false);
+        l1_odd(0);
+        l1_rest();
+        for (int c = 1; c < nch1; ++c) {
+            begin(n4);
+            overlap(fa, fb, false, 0, s0, s1);
+            epilogue_l1(c - 1, full);
+            clear();
+            adv(false);
+            l1_odd(0);
+            l1_rest();
+        }
+        // L2 phase; its first step closes L1: the last L1 MFMAs and epilogue,
+        // every wave's activations in LDS, then the first L2 reads
+        begin_l2(n2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mfma_tile(fb, i, s1, full);
+        epilogue_l1(nch1 - 1, full);
+        clear();
+        lds_reads_done_barrier();
+#pragma unroll
+        for (int p = 0; p < 5; ++p) read_piece(fa, p, true, sst, rsc, 0, 0, full);
+        adv(false);
+        l2_odd(0);
+        l2_rest();
+        for (int c = 1; c < nch2; ++c) {
+            begin_l2(n2);
+            overlap(fa, fb, true, 0, s0, s1);
+            epilogue_l2(c - 1);
+            e1 = true;
+            clear();
+            adv(false);
+            l2_odd(0);
+            l2_rest();
+        }
+        // the last step's MFMAs and the last L2 chunk's epilogue
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mfma_tile(fb, i, s1, full);
+        epilogue_l2(nch2 - 1);
+    };
+    if (nrt == 4)
+        stream(std::true_type{});
+    else
+        stream(std::false_type{});
+    wait_all_loads();
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_l1(GemmArgs args) {
@@ -1450,6 +1942,11 @@ __global__ __launch_bounds__(kGemmThreads, kDecWorkgroupsPerCU) void k_gemm_l1_t
 __global__ __launch_bounds__(kGemmThreads, kDecWorkgroupsPerCU) void k_gemm_l2_t128(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) uint8_t st[dec_stages(2) * dec_stage_bytes(2)];
     gemm_decode<kL2, 2>(args, st, nullptr);
+}
+
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_fused(GemmArgs l1, GemmArgs l2) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kFusedLds];
+    gemm_fused(l1, l2, lds);
 }
 
 // One 16-byte chunk per thread, in the order of the tile-blocked layout

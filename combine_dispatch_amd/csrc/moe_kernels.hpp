@@ -46,6 +46,13 @@ constexpr int dec_stages(int rm) { return rm == 1 ? 3 : 2; }
 static_assert(kDecWorkgroupsPerCU * dec_stages(1) * dec_stage_bytes(1) <= 160 * 1024, "LDS");
 static_assert(kDecWorkgroupsPerCU * dec_stages(2) * dec_stage_bytes(2) <= 160 * 1024, "LDS");
 
+// L1 and L2 in one launch: one workgroup per m-tile of at most kFusedRows
+// rows (the second tile table, written with kFusedRows-row tiles), which
+// keeps the tile's e4m3 activations (I <= kFusedMaxI columns) and their scale
+// words in LDS between the two GEMMs.
+constexpr int kFusedRows = 128;
+constexpr int kFusedMaxI = 768;
+
 // Tile records a persistent GEMM workgroup keeps in LDS: the launch must give
 // no workgroup more tiles than this (at most ceil(ceil(tiles / 8) / (grid / 8))).
 constexpr int kTileCache = 256;
@@ -170,6 +177,10 @@ constexpr int kBTileBytes = kBN * kBK / 2;
 __global__ void k_pack_weights_tiled(const uint8_t* __restrict__ W, uint8_t* __restrict__ Wp, int E,
                                      int N, int Kdim, int I, int l1);
 __global__ void k_gemm_l1(GemmArgs args);
+// l1: the L1 GEMM's arguments (mtiles / num_mtiles: the kFusedRows-row
+// table; act_q / act_s unused); l2: the L2 GEMM's B, SB, Kdim = I, N = H,
+// ntiles = H / 256, out.
+__global__ void k_gemm_fused(GemmArgs l1, GemmArgs l2);
 __global__ void k_gemm_l2(GemmArgs args);
 __global__ void k_gemm_l1_decode(GemmArgs args);
 __global__ void k_gemm_l2_decode(GemmArgs args);

@@ -67,13 +67,27 @@ typedef struct {
                                  MOE_TILES_PERSISTENT: 256-row tiles, one
                                  workgroup per CU working through its tiles;
                                  MOE_TILES_64 / MOE_TILES_128: 64- or 128-row
-                                 tiles, one workgroup each.  The last two need
-                                 the one-launch routing (ceil(T*K/1024) * E <=
+                                 tiles, one workgroup each;
+                                 MOE_TILES_FUSED: L1 and L2 in one launch, one
+                                 workgroup per 128-row tile keeping the tile's
+                                 e4m3 activations and their scales in LDS
+                                 between the two GEMMs ([P1] "L1 Epilogue"
+                                 snippet: the SwiGLU output stays in shared
+                                 memory as the L2 input); needs I <= 768, and
+                                 the workspace's act_q / act_s views are then
+                                 not written.  The last three need the
+                                 one-launch routing (ceil(T*K/1024) * E <=
                                  65536), else MOE_ERR_UNSUPPORTED; any other
                                  value -> MOE_ERR_INVALID_ARG */
 } moe_options_t;
 
-enum { MOE_TILES_AUTO = 0, MOE_TILES_PERSISTENT = 1, MOE_TILES_64 = 2, MOE_TILES_128 = 3 };
+enum {
+    MOE_TILES_AUTO = 0,
+    MOE_TILES_PERSISTENT = 1,
+    MOE_TILES_64 = 2,
+    MOE_TILES_128 = 3,
+    MOE_TILES_FUSED = 4
+};
 
 enum {
     MOE_OK = 0,

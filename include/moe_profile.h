@@ -32,8 +32,9 @@ enum {
     MOE_STAGE_POOL_SCALES,     /* a4: the pool rows' scale words gathered by token (empty when
                                   the L1 GEMM reads them by token: the 64-row-tile GEMMs
                                   with at most 1024 routed slots) */
-    MOE_STAGE_GEMM_L1,         /* a5-a7: L1 GEMM (gathers the token rows), SwiGLU*w, e4m3 requant */
-    MOE_STAGE_GEMM_L2,         /* a8: L2 GEMM, bf16 rows */
+    MOE_STAGE_GEMM_L1,         /* a5-a7: L1 GEMM (gathers the token rows), SwiGLU*w, e4m3 requant;
+                                  with gemm_tiles = MOE_TILES_FUSED also a8 (one launch) */
+    MOE_STAGE_GEMM_L2,         /* a8: L2 GEMM, bf16 rows (empty with MOE_TILES_FUSED) */
     MOE_STAGE_COMBINE,         /* a9: top-k fp32 reduction to bf16 */
     MOE_PROFILE_STAGES
 };

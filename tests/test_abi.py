@@ -110,10 +110,15 @@ def test_host_side_errors_need_no_device(moe):
     # dereference (the pointers below are never touched)
     big = moe.MoeShape(8192, 256, 128, 1024, 16)
     fake = ctypes.c_void_p(1 << 20)
-    for tiles in (moe.MOE_TILES_64, moe.MOE_TILES_128):
+    for tiles in (moe.MOE_TILES_64, moe.MOE_TILES_128, moe.MOE_TILES_FUSED):
         o = moe.options(gemm_tiles=tiles)
         assert L.moe_fused_forward(ctypes.byref(big), ctypes.byref(o), *[fake] * 8, fake, 1 << 40,
                                    null) == moe.MOE_ERR_UNSUPPORTED
+    # L1 and L2 in one launch keeps a 128 x I activation tile in LDS: I <= 768
+    o = moe.options(gemm_tiles=moe.MOE_TILES_FUSED)
+    wide = moe.MoeShape(64, 256, 896, 8, 2)
+    assert L.moe_fused_forward(ctypes.byref(wide), ctypes.byref(o), *[fake] * 8, fake, 1 << 40,
+                               null) == moe.MOE_ERR_UNSUPPORTED
     # unknown payload
     assert L.moe_dispatch(ctypes.byref(s), null, null, null, 7, *[null] * 7, null, 0,
                           null) == moe.MOE_ERR_INVALID_ARG

@@ -172,6 +172,23 @@ def explain_worst_token(inp, r, y, y_ref, gq, gs, rq, rs, l2, o_ref):
             f"|o_ref| {np.linalg.norm(orf):.4e}, |o_gpu - o_ref| {np.linalg.norm(og - orf):.4e}")
 
 
+def check_fused(inp, dev, pw, y, ws_ref):
+    """The layer with L1 and L2 in one launch (the activation tile kept in
+    LDS) gives the same y and the same bf16 L2 rows, bit for bit, as the
+    separate GEMMs whose results the oracle checked."""
+    import combine_dispatch_amd as moe
+    T, H, I, E, K = (inp[k] for k in ("T", "H", "I", "E", "K"))
+    ws = torch.empty(moe.moe_workspace_bytes(T, H, I, E, K), dtype=torch.uint8, device=DEV)
+    yf = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    moe.moe_fused_forward_prepacked(dev["x"], dev["topk_idx"], dev["topk_w"], pw, yf, ws, E=E, I=I,
+                                    opts=moe.options(gemm_tiles=moe.MOE_TILES_FUSED))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bf16_bits(yf), y)
+    R = int(view(ws_ref, inp, "offsets")[-1])
+    np.testing.assert_array_equal(view(ws, inp, "l2_out", R), view(ws_ref, inp, "l2_out", R))
+    say("L1 + L2 in one launch: y and every L2 row bit-identical")
+
+
 # full compares: every routed row
 FULL_CASES = {
     # the small-batch workload
@@ -212,6 +229,8 @@ def test_full_compare(name):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bf16_bits(yp), y)
     say(name, "prepacked-weight entry bit-identical")
+    if I <= 768:
+        check_fused(inp, dev, pw, y, ws)
 
 
 @pytest.mark.parametrize("name", ["prefill", "skewed", "many"])
@@ -239,3 +258,5 @@ def test_workload_tile_edges(name):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(bf16_bits(yp), y)
     say(name, "prepacked-weight entry bit-identical")
+    if I <= 768:
+        check_fused(inp, dev, pw, y, ws)

@@ -182,6 +182,14 @@ def test_gemm_tile_kernels_agree(case):
         for n in m0:
             np.testing.assert_array_equal(m[n], m0[n], err_msg=f"{n}, gemm_tiles {tiles}")
         np.testing.assert_array_equal(y, y0, err_msg=f"y, gemm_tiles {tiles}")
+    # L1 and L2 in one launch (activations kept in LDS, so the workspace's
+    # act_q / act_s are not written): the same L2 rows and y
+    if inp["I"] <= 768:
+        say("gemm_tiles fused")
+        y, ws = run_forward(inp, dev, opts=moe.options(gemm_tiles=moe.MOE_TILES_FUSED))
+        R = int(view(ws, inp, "offsets")[-1])
+        np.testing.assert_array_equal(view(ws, inp, "l2_out", R), m0["l2_out"], err_msg="l2_out, fused")
+        np.testing.assert_array_equal(y, y0, err_msg="y, fused")
     # and the common result is the oracle's, to the layer's bars
     y_ref = oracle.forward(inp)
     check_y(y0, y_ref, inp["topk_idx"])
@@ -443,6 +451,15 @@ def test_prepacked_weights(case):
         np.testing.assert_array_equal(bf16_bits(y), y_ref)
         for name in ("act_q", "act_s", "l2_out"):
             np.testing.assert_array_equal(view(ws, inp, name, R), view(ws_ref, inp, name, R))
+    if I <= 768:
+        say("gemm_tiles fused")
+        ws = torch.empty(moe.moe_workspace_bytes(T, H, I, E, K), dtype=torch.uint8, device=DEV)
+        y = torch.empty((T, H), dtype=torch.int16, device=DEV)
+        moe.moe_fused_forward_prepacked(dev["x"], dev["topk_idx"], dev["topk_w"], packed, y, ws, E=E, I=I,
+                                        opts=moe.options(gemm_tiles=moe.MOE_TILES_FUSED))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bf16_bits(y), y_ref)
+        np.testing.assert_array_equal(view(ws, inp, "l2_out", R), view(ws_ref, inp, "l2_out", R))
     short = torch.empty(nbytes - 256, dtype=torch.uint8, device=DEV)
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_pack_weights(dev["W1q"], dev["S1"], dev["W2q"], dev["S2"], short, E=E, H=H, I=I)

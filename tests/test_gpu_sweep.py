@@ -51,7 +51,10 @@ def test_sweep_case(case):
     yo = torch.empty((T, H), dtype=torch.int16, device=DEV)
     pw = torch.empty(moe.moe_packed_weights_bytes(H, I, E), dtype=torch.uint8, device=DEV)
     moe.moe_pack_weights(dev["W1q"], dev["S1"], dev["W2q"], dev["S2"], pw, E=E, H=H, I=I)
-    for tiles in (moe.MOE_TILES_AUTO, moe.MOE_TILES_PERSISTENT, moe.MOE_TILES_64, moe.MOE_TILES_128):
+    families = [moe.MOE_TILES_AUTO, moe.MOE_TILES_PERSISTENT, moe.MOE_TILES_64, moe.MOE_TILES_128]
+    if I <= 768:
+        families.append(moe.MOE_TILES_FUSED)  # L1 and L2 in one launch
+    for tiles in families:
         moe.moe_fused_forward_prepacked(dev["x"], dev["topk_idx"], dev["topk_w"], pw, yo, ws, E=E, I=I,
                                         opts=moe.options(gemm_tiles=tiles))
         torch.cuda.synchronize()
