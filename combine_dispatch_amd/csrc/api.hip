@@ -532,7 +532,7 @@ int fused_forward(const moe_shape_t* s, const moe_options_t* opt, const void* x,
         }
         g1.mtiles = reinterpret_cast<const MTile*>(ws + L.mtiles64);
         g1.num_mtiles = reinterpret_cast<const int32_t*>(ws + L.num_mtiles64);
-        hipLaunchKernelGGL(plan.rm == 1 ? k_gemm_l1_decode : k_gemm_l1_t128,
+        hipLaunchKernelGGL(plan.rm == 1 ? (b_tiled ? k_gemm_l1_decode_nt : k_gemm_l1_decode) : k_gemm_l1_t128,
                            dim3(dec_grid_rows * (unsigned)g1.ntiles), dim3(kGemmThreads), 0, stream, g1);
     } else {
         hipLaunchKernelGGL(k_gemm_l1, dim3(gemm_grid(L.max_mtiles * g1.ntiles)), dim3(kGemmThreads), 0,

@@ -183,6 +183,9 @@ __global__ void k_gemm_l1(GemmArgs args);
 __global__ void k_gemm_fused(GemmArgs l1, GemmArgs l2);
 __global__ void k_gemm_l2(GemmArgs args);
 __global__ void k_gemm_l1_decode(GemmArgs args);
+// the same for tile-blocked weights (b_tiled), whose blocks it streams with
+// the non-temporal hint
+__global__ void k_gemm_l1_decode_nt(GemmArgs args);
 __global__ void k_gemm_l2_decode(GemmArgs args);
 __global__ void k_gemm_l1_t128(GemmArgs args);
 __global__ void k_gemm_l2_t128(GemmArgs args);
