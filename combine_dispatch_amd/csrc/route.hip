@@ -860,6 +860,8 @@ __global__ __launch_bounds__(256) void k_dispatch_bf16(const uint16_t* __restric
 // in flight per lane, the rate of a plain HBM read stream), then summed in
 // ascending k in fp32 starting from +0, then rounded to bf16.  Multiplies and
 // adds stay separately rounded.
+// 2048-column chunks per lane per pass (each with its K rows' loads in flight)
+constexpr int kCH = 4;
 #pragma clang fp contract(off)
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
                                                 const int32_t* __restrict__ slot_to_pool,
@@ -883,24 +885,24 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
     const int span = tpb * H;
     const int piece = ((span + nparts - 1) / nparts + 7) & ~7;
     const int lo = part * piece, hi = min(span, lo + piece);
-    for (int c00 = lo + threadIdx.x * 8; c00 < hi; c00 += 4 * 256 * 8) {
-        int tok[4], col[4];
+    for (int c00 = lo + threadIdx.x * 8; c00 < hi; c00 += kCH * 256 * 8) {
+        int tok[kCH], col[kCH];
 #pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
+        for (int hh = 0; hh < kCH; ++hh) {
             const int p = c00 + hh * 256 * 8;
             const int j = p < hi ? p / H : -1;  // H % 8 == 0: a lane's 8 columns share a token
             tok[hh] = j;
             col[hh] = j >= 0 ? p - j * H : 0;
         }
-        float acc[4][8];
+        float acc[kCH][8];
 #pragma unroll
-        for (int hh = 0; hh < 4; ++hh)
+        for (int hh = 0; hh < kCH; ++hh)
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[hh][j] = 0.0f;
         for (int k0 = 0; k0 < K; k0 += 8) {
-            u32x4 v[4][8];
+            u32x4 v[kCH][8];
 #pragma unroll
-            for (int hh = 0; hh < 4; ++hh) {
+            for (int hh = 0; hh < kCH; ++hh) {
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const int k = k0 + u;
@@ -913,7 +915,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
                 }
             }
 #pragma unroll
-            for (int hh = 0; hh < 4; ++hh) {
+            for (int hh = 0; hh < kCH; ++hh) {
                 if (tok[hh] < 0) continue;
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
@@ -938,7 +940,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o,
             }
         }
 #pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
+        for (int hh = 0; hh < kCH; ++hh) {
             if (tok[hh] < 0 || t0 + tok[hh] >= T) continue;
             const u32x4 out = {pack_bf16x2(acc[hh][0], acc[hh][1]), pack_bf16x2(acc[hh][2], acc[hh][3]),
                                pack_bf16x2(acc[hh][4], acc[hh][5]), pack_bf16x2(acc[hh][6], acc[hh][7])};

@@ -1,6 +1,7 @@
 """Builds tests/probe/libmfma_block.so (the one-block scaled-MFMA probe that a
-GPU regression test compares with exact sums) with hipcc for gfx950.  Test
-infrastructure, run on the CPU by the build step."""
+GPU regression test compares with exact sums, the MFMA-rate probe and the
+HBM read-rate probe) with hipcc for gfx950.  Test infrastructure, run on the
+CPU by the build step."""
 from __future__ import annotations
 
 import os

@@ -2,7 +2,8 @@
 // (v_mfma_scale_f32_32x32x64_f8f6f4, A = e4m3, B = e2m1, one UE8M0 scale per
 // 32 along K on each operand) per 32 x 32 x 64 block, with a zero
 // accumulator, so that a test can compare each block's result with the exact
-// sum of its products.  Not part of the layer library.
+// sum of its products; also the MFMA-rate and HBM read-rate probes.  Not part
+// of the layer library.
 //
 // Operand lane layout (the same one the layer's GEMMs use):
 //  A (8 VGPRs): lane l holds row l%32; bytes 0-15 are k = 16*(l/32)+0..15,
@@ -134,4 +135,42 @@ extern "C" float mfma_rate_run(int fmt_b, int random, int iters, int blocks, voi
     hipEventDestroy(e0);
     hipEventDestroy(e1);
     return ms;
+}
+
+// ---------------------------------------------------------------------------
+// HBM read-stream rate: each workgroup reads one contiguous span of a buffer
+// with 16-byte loads, eight per lane in flight, with or without the
+// non-temporal hint, and folds the data so the loads stay.  Gives the read
+// rate a streaming kernel reaches, beside the 8 TB/s peak.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <bool NT>
+__global__ __launch_bounds__(256) void k_hbm_read(const u32x4_t* __restrict__ p, size_t n16, size_t per_block,
+                                                  unsigned* __restrict__ out) {
+    const size_t base = (size_t)blockIdx.x * per_block;
+    unsigned acc = 0;
+    for (size_t i = base + threadIdx.x; i < base + per_block; i += 256 * 8) {
+        u32x4_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const size_t j = i + (size_t)u * 256;
+            v[u] = j < n16 ? (NT ? __builtin_nontemporal_load(p + j) : p[j]) : u32x4_t{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    if (acc == 0x9E3779B9u) out[blockIdx.x] = acc;  // practically never: keeps the loads
+}
+
+// bytes must be a multiple of 16 * blocks; out holds at least `blocks` words.
+extern "C" int hbm_read_run(const void* p, size_t bytes, int blocks, int nt, void* out, void* stream) {
+    const size_t n16 = bytes / 16;
+    if (blocks <= 0 || bytes % 16 || n16 % (size_t)blocks) return -1;
+    const size_t per = n16 / blocks;
+    const u32x4_t* P = static_cast<const u32x4_t*>(p);
+    unsigned* O = static_cast<unsigned*>(out);
+    if (nt)
+        hipLaunchKernelGGL(k_hbm_read<true>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, P, n16, per, O);
+    else
+        hipLaunchKernelGGL(k_hbm_read<false>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, P, n16, per, O);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
 }
