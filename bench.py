@@ -282,13 +282,15 @@ def main():
     # routed slots per expert on average
     l1_kernel = {"64": "gemm_l1_decode", "128": "gemm_l1_t128", "persistent": "gemm_l1"}.get(
         a.gemm_tiles, "gemm_l1_decode" if T * K <= 64 * E else "gemm_l1")
+    if l1_kernel == "gemm_l1_decode" and a.weights == "prepacked":
+        l1_kernel = "gemm_l1_decode_nt"  # its variant for tile-blocked weights
     # L1 algorithmic bytes: W1 codes and scales of every expert that holds a
     # routed row, the token rows' codes once, the A-scale words (by token in
     # the 64-row-tile GEMM up to 1024 routed slots, else per routed row), each
     # routed row's weight and token index, the e4m3 activations and their
     # scales
     experts_used = int(np.unique(inp["topk_idx"][inp["topk_idx"] >= 0]).size)
-    a_scale_rows = T if (l1_kernel == "gemm_l1_decode" and T * K <= 1024) else R
+    a_scale_rows = T if (l1_kernel.startswith("gemm_l1_decode") and T * K <= 1024) else R
     l1_bytes = (experts_used * 2 * I * (H // 2 + H // 32) + T * H + a_scale_rows * (H // 32) + R * 8
                 + R * (I + I // 32))
     if a.gemm_tiles == "fused":
