@@ -470,5 +470,14 @@ def test_exact_math_option_also_within_tolerance():
     import combine_dispatch_amd as moe
     inp = small_inputs(SMALL[1])
     y_ref = oracle.forward(inp)
-    y, _ = run_forward(inp, opts=moe.options(fast_math=False))
+    y, ws = run_forward(inp, opts=moe.options(fast_math=False))
     check_y(y, y_ref, inp["topk_idx"])
+    # every GEMM kernel family takes the same exact-math epilogue: the same bits
+    R = int(view(ws, inp, "offsets")[-1])
+    l2 = view(ws, inp, "l2_out", R).copy()
+    dev = to_dev(inp)
+    for tiles in (moe.MOE_TILES_PERSISTENT, moe.MOE_TILES_64, moe.MOE_TILES_128, moe.MOE_TILES_FUSED):
+        say("gemm_tiles", tiles)
+        yt, wt = run_forward(inp, dev, opts=moe.options(fast_math=False, gemm_tiles=tiles))
+        np.testing.assert_array_equal(yt, y, err_msg=f"y, exact math, gemm_tiles {tiles}")
+        np.testing.assert_array_equal(view(wt, inp, "l2_out", R), l2, err_msg=f"l2_out, gemm_tiles {tiles}")
